@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for decode attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg
+import this package; the HIP library and its Python binding never do.
+"""
+
+from .fp64 import (  # noqa: F401
+    attention,
+    bifurcated_attention,
+    default_scale,
+    lse_combine,
+    split_partials,
+)

@@ -1,0 +1,136 @@
+"""The fp64 oracle against its pins (CPU only), plus planted-mistake checks.
+
+The mutation tests plant one plausible mistake at a time in a copy of the
+oracle (on the CPU) and require that at least one pin catches it.
+"""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp64 as oa
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)
+
+
+def _mutant(**overrides):
+    """A namespace like the oracle package with some functions replaced."""
+    ns = types.SimpleNamespace(
+        attention=oa.attention, bifurcated_attention=oa.bifurcated_attention,
+        split_partials=oa.split_partials, lse_combine=oa.lse_combine,
+        default_scale=oa.default_scale)
+    for name, fn in overrides.items():
+        setattr(ns, name, fn)
+    return ns
+
+
+def _with_rows(rows_fn):
+    """Rebuild attention/bifurcated/split_partials over a broken row kernel."""
+    saved = oa._attend_rows
+
+    def wrap(fn):
+        def inner(*a, **kw):
+            oa._attend_rows = rows_fn
+            try:
+                return fn(*a, **kw)
+            finally:
+                oa._attend_rows = saved
+        return inner
+
+    return _mutant(attention=wrap(oa.attention), bifurcated_attention=wrap(oa.bifurcated_attention),
+                   split_partials=wrap(oa.split_partials))
+
+
+def _rows_no_scale(q, k, v, scale):
+    return oa.__dict__["_attend_rows_ref"](q, k, v, 1.0)
+
+
+def _rows_log2_lse(q, k, v, scale):
+    o, l = oa._attend_rows_ref(q, k, v, scale)
+    return o, l / np.log(2.0)
+
+
+def _rows_no_normalise(q, k, v, scale):
+    if k.shape[0] == 0:
+        return oa._attend_rows_ref(q, k, v, scale)
+    s = scale * (q @ k.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e @ v, m[:, 0] + np.log(e.sum(axis=1))
+
+
+def _rows_keys_for_values(q, k, v, scale):
+    return oa._attend_rows_ref(q, k, k, scale)
+
+
+def _rows_drop_last(q, k, v, scale):
+    return oa._attend_rows_ref(q, k[:-1] if k.shape[0] > 1 else k, v[:-1] if v.shape[0] > 1 else v, scale)
+
+
+def _rows_wrong_sign(q, k, v, scale):
+    return oa._attend_rows_ref(q, k, v, -scale)
+
+
+def _attention_interleaved_gqa(q, k, v, lens=None, scale=None):
+    # query head h reads KV head h % Hkv instead of h // G
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    perm = np.array([(h % Hkv) * G + h // Hkv for h in range(Hq)])
+    out, lse = oa.attention(q[:, np.argsort(perm)], k, v, lens, scale)
+    return out[:, perm], lse[:, perm]
+
+
+def _combine_wrong_sign(o_part, lse_part):
+    o_part = np.asarray(o_part, dtype=np.float64)
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    M = lse_part.max(axis=0)
+    w = np.where(np.isneginf(lse_part), 0.0, np.exp(M - lse_part))
+    z = w.sum(axis=0)
+    return (w[..., None] * o_part).sum(axis=0) / z[..., None], M + np.log(z)
+
+
+def _combine_plain_mean(o_part, lse_part):
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    live = ~np.isneginf(lse_part)
+    o = (np.asarray(o_part) * live[..., None]).sum(axis=0) / live.sum(axis=0)[..., None]
+    return o, lse_part.max(axis=0)
+
+
+MUTANTS = {
+    "dropped_scale": lambda: _with_rows(_rows_no_scale),
+    "lse_in_log2": lambda: _with_rows(_rows_log2_lse),
+    "missing_normalisation": lambda: _with_rows(_rows_no_normalise),
+    "keys_used_as_values": lambda: _with_rows(_rows_keys_for_values),
+    "off_by_one_rows": lambda: _with_rows(_rows_drop_last),
+    "wrong_score_sign": lambda: _with_rows(_rows_wrong_sign),
+    "interleaved_gqa": lambda: _mutant(attention=_attention_interleaved_gqa),
+    "combine_wrong_sign": lambda: _mutant(lse_combine=_combine_wrong_sign),
+    "combine_unweighted": lambda: _mutant(lse_combine=_combine_plain_mean),
+}
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _keep_reference_rows():
+    oa._attend_rows_ref = oa._attend_rows
+    yield
+    del oa._attend_rows_ref
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    orc = MUTANTS[name]()
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,76 @@
+"""The five decode-attention workloads, as plain shapes and seeds.
+
+Each workload is stated by what it is and its sizes.  Seeds: workload k uses
+seed k for its tensors; point j of a sweep uses 100*k + j.
+"""
+
+from dataclasses import dataclass
+
+__all__ = ["DecodeWorkload", "BifurcatedWorkload", "TINY", "CODELLAMA34B_SHARE",
+           "MHA_SWEEP", "BIFURCATED_MQA", "BIFURCATED_GQA", "ALL_DECODE", "ALL_BIFURCATED"]
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    max_len: int
+    dtype: str                 # 'bf16' or 'fp32' (q, K, V storage)
+    ragged: bool               # lens uniform in [max_len/2, max_len] when True
+    n_splits: int              # <= 0: split count chosen by the planner
+    seed: int
+    tol: float                 # max-abs error bound against the fp64 oracle
+
+    def kv_bytes_allocated(self):
+        sz = 2 if self.dtype == "bf16" else 4
+        return 2 * self.batch * self.kv_heads * self.max_len * self.head_dim * sz
+
+
+@dataclass(frozen=True)
+class BifurcatedWorkload:
+    name: str
+    samples: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    ctx_len: int
+    dec_max: int
+    dec_lo: int                # dec_lens uniform in [dec_lo, dec_max]
+    dtype: str
+    seed: int
+    tol: float
+
+
+# Tiny check case: batch 1, 4 query heads = 4 KV heads, D 64, 512 tokens,
+# fp32, 4 KV splits.
+TINY = DecodeWorkload("tiny_b1_h4_d64_l512_fp32", 1, 4, 4, 64, 512, "fp32",
+                      False, 4, 1, 1e-5)
+
+# One GPU's quarter-of-heads share of a CodeLlama-34B layer: 16 query heads
+# over 2 KV heads (GQA 8:1), D 128, 65536 cached tokens, batch 1, bf16.
+CODELLAMA34B_SHARE = DecodeWorkload("codellama34b_share_b1_hq16_hkv2_d128_l65536_bf16",
+                                    1, 16, 2, 128, 65536, "bf16", False, 0, 2, 1e-2)
+
+# MHA length sweep: 32 heads = 32 KV heads, D 128, bf16, ragged lengths
+# uniform in [L/2, L], L in {512, 2K, 8K, 32K, 64K}, batch 1 and 16.
+MHA_SWEEP = tuple(
+    DecodeWorkload(f"mha_b{B}_h32_d128_l{L}_bf16", B, 32, 32, 128, L, "bf16", True, 0,
+                   100 * 3 + j, 1e-2)
+    for j, (L, B) in enumerate((L, B) for L in (512, 2048, 8192, 32768, 65536) for B in (1, 16))
+)
+
+# Bifurcated MQA: 64 samples share an 8192-token context, each with 256 decode
+# tokens; 32 query heads over 1 KV head, D 128, bf16.
+BIFURCATED_MQA = BifurcatedWorkload("bifurcated_mqa_s64_ctx8192_dec256_hq32_hkv1_d128_bf16",
+                                    64, 32, 1, 128, 8192, 256, 256, "bf16", 4, 1e-2)
+
+# Bifurcated GQA: 128 samples share a 32768-token context; decode lengths
+# uniform in [1, 512]; 32 query heads over 8 KV heads, D 128, bf16.
+BIFURCATED_GQA = BifurcatedWorkload("bifurcated_gqa_s128_ctx32768_dec1to512_hq32_hkv8_d128_bf16",
+                                    128, 32, 8, 128, 32768, 512, 1, "bf16", 5, 1e-2)
+
+ALL_DECODE = (TINY, CODELLAMA34B_SHARE) + MHA_SWEEP
+ALL_BIFURCATED = (BIFURCATED_MQA, BIFURCATED_GQA)

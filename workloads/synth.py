@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module draws numbers and nothing else: it holds none of the attention
+arithmetic, and neither the oracle nor the HIP binding imports it.
+
+Distribution (the same for every workload): q, K and V entries are i.i.d.
+N(0, 1) drawn in float32; bf16 workloads round each draw to the nearest bf16
+value (ties to even).  Ragged lengths are integers drawn uniformly from an
+inclusive range.  Cache rows beyond a sequence's length are padding; parity
+runs fill them with NaN so that any read of them poisons the result.
+"""
+
+import numpy as np
+
+__all__ = [
+    "round_to_bf16",
+    "host_normal",
+    "host_lengths",
+    "decode_case",
+    "bifurcated_case",
+    "device_normal",
+    "device_lengths",
+]
+
+
+def round_to_bf16(x):
+    """float32 array -> float32 array holding the nearest bf16 values (RNE).
+
+    bf16 keeps the top 16 bits of an IEEE float32; rounding to nearest-even
+    adds 0x7FFF plus the lowest kept bit before truncating.  NaN stays NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    r = r.astype(np.uint32)
+    out = r.view(np.float32).copy()
+    nan = np.isnan(x)
+    out[nan] = np.float32(np.nan)
+    return out
+
+
+def host_normal(shape, seed, dtype="bf16"):
+    """N(0,1) float32 draws from PCG64(seed), bf16-rounded for dtype 'bf16'."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "bf16":
+        x = round_to_bf16(x)
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return x
+
+
+def host_lengths(count, lo, hi, seed):
+    """`count` integers uniform in [lo, hi] (both ends included)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.integers(lo, hi + 1, size=count, dtype=np.int64)
+
+
+def decode_case(B, Hq, Hkv, D, Lmax, dtype, seed, lens=None, pad_nan=True):
+    """Host inputs for one decode-attention call.
+
+    Returns dict(q [B,Hq,D], k, v [B,Hkv,Lmax,D] float32 arrays holding the
+    exact input values, lens [B] int32).  lens=None means every sequence is
+    Lmax long; a (lo, hi) tuple draws ragged lengths from seed + 7.
+    """
+    q = host_normal((B, Hq, D), seed, dtype)
+    k = host_normal((B, Hkv, Lmax, D), seed + 1, dtype)
+    v = host_normal((B, Hkv, Lmax, D), seed + 2, dtype)
+    if lens is None:
+        lens = np.full(B, Lmax, dtype=np.int64)
+    elif isinstance(lens, tuple):
+        lens = host_lengths(B, lens[0], lens[1], seed + 7)
+    lens = np.asarray(lens, dtype=np.int64)
+    if pad_nan:
+        for b in range(B):
+            k[b, :, lens[b]:, :] = np.nan
+            v[b, :, lens[b]:, :] = np.nan
+    return {"q": q, "k": k, "v": v, "lens": lens.astype(np.int32)}
+
+
+def bifurcated_case(S, Hq, Hkv, D, Lc, Ldmax, dtype, seed, dec_lens=None, pad_nan=True):
+    """Host inputs for one bifurcated call.
+
+    Returns dict(q [S,Hq,D], k_ctx, v_ctx [Hkv,Lc,D], k_dec, v_dec
+    [S,Hkv,Ldmax,D], dec_lens [S] int32).  dec_lens: None = all Ldmax, a
+    (lo, hi) tuple = uniform draw from seed + 7, or an explicit sequence.
+    """
+    q = host_normal((S, Hq, D), seed, dtype)
+    kc = host_normal((Hkv, Lc, D), seed + 1, dtype)
+    vc = host_normal((Hkv, Lc, D), seed + 2, dtype)
+    kd = host_normal((S, Hkv, Ldmax, D), seed + 3, dtype)
+    vd = host_normal((S, Hkv, Ldmax, D), seed + 4, dtype)
+    if dec_lens is None:
+        dec_lens = np.full(S, Ldmax, dtype=np.int64)
+    elif isinstance(dec_lens, tuple):
+        dec_lens = host_lengths(S, dec_lens[0], dec_lens[1], seed + 7)
+    dec_lens = np.asarray(dec_lens, dtype=np.int64)
+    if pad_nan:
+        for s in range(S):
+            kd[s, :, dec_lens[s]:, :] = np.nan
+            vd[s, :, dec_lens[s]:, :] = np.nan
+    return {"q": q, "k_ctx": kc, "v_ctx": vc, "k_dec": kd, "v_dec": vd,
+            "dec_lens": dec_lens.astype(np.int32)}
+
+
+def device_normal(shape, seed, dtype, device):
+    """N(0,1) draws made on the device by torch's seeded generator.
+
+    Used where the host cannot draw the data in reasonable time (the
+    multi-GiB caches); the exact bits are copied back wherever the oracle
+    needs them.  dtype is 'bf16' or 'fp32'.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.empty(shape, dtype=torch.float32, device=device)
+    x.normal_(0.0, 1.0, generator=g)
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    return x
+
+
+def device_lengths(count, lo, hi, seed, device):
+    """host_lengths() moved to the device as int32."""
+    import torch
+
+    return torch.tensor(host_lengths(count, lo, hi, seed), dtype=torch.int32, device=device)
