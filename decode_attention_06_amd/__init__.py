@@ -1,0 +1,220 @@
+"""Python binding of libfd (MI355X decode attention): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI in
+include/fd.h.  PyTorch supplies device memory and the current stream; this
+module checks tensor shapes, dtypes and placement, allocates the workspace
+with torch, and calls the library through ctypes.  If libfd.so has not been
+built the first call raises: there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfd.so")
+
+FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
+FD_F32, FD_BF16 = 0, 1
+FD_MAX_SPLITS = 4096
+
+# Exported symbols and their ctypes signatures (mirrors include/fd.h).
+_c_i32, _c_i64, _c_sz, _c_vp, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "fd_status_string": (ctypes.c_char_p, [_c_i32]),
+    "fd_last_error_message": (ctypes.c_char_p, []),
+    "fd_version": (_c_i32, []),
+    "fd_plan_splits": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32]),
+    "fd_device_cu_count": (_c_i32, [ctypes.POINTER(_c_i32)]),
+    "fd_decode_attn_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+                                               ctypes.POINTER(_c_sz)]),
+    "fd_decode_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_bifurcated_attn_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
+                                                   ctypes.POINTER(_c_sz)]),
+    "fd_bifurcated_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    _c_i64, _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_lse_combine": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
+}
+
+_lib = None
+
+
+class FdError(RuntimeError):
+    """A non-OK fd_status, with the library's message."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+def load(path=LIB_PATH):
+    """Load libfd.so (once) and attach the ctypes signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with `python -m decode_attention_06_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(status):
+    return load().fd_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != FD_OK:
+        raise FdError(status, load().fd_last_error_message().decode())
+
+
+def plan_splits(batch, q_heads, kv_heads, head_dim, max_len, dtype, n_cu):
+    """fd_plan_splits: host-only split planner (-1 for invalid arguments)."""
+    return load().fd_plan_splits(batch, q_heads, kv_heads, head_dim, max_len, dtype, n_cu)
+
+
+def device_cu_count():
+    n = _c_i32(0)
+    _check(load().fd_device_cu_count(ctypes.byref(n)))
+    return n.value
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FD_F32
+    if t.dtype == torch.bfloat16:
+        return FD_BF16
+    raise FdError(FD_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported (float32 or bfloat16)")
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise FdError(FD_ERR_INVALID_ARG, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise FdError(FD_ERR_INVALID_ARG, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _opt_ptr(t, name):
+    return None if t is None else _dev_ptr(t, name)
+
+
+def decode_workspace_size(batch, q_heads, kv_heads, head_dim, max_len, dtype, n_splits=0):
+    n = _c_sz(0)
+    _check(load().fd_decode_attn_workspace_size(batch, q_heads, kv_heads, head_dim, max_len, dtype,
+                                                n_splits, ctypes.byref(n)))
+    return n.value
+
+
+def decode_attn(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=0.0,
+                return_lse=False, workspace=None, stream=None):
+    """Split-KV decode attention (fd_decode_attn).
+
+    q [B, Hq, D]; k, v [B, Hkv, Lmax, D] (same dtype: float32 or bfloat16);
+    lens int32 [B] on the device or None.  Returns out [B, Hq, D] (dtype of q
+    unless out/out_dtype say otherwise), and the natural-log lse [B, Hq]
+    float32 when return_lse.
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise FdError(FD_ERR_INVALID_ARG, "expected q [B,Hq,D] and k, v [B,Hkv,Lmax,D]")
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, Dk = k.shape
+    if k.shape[0] != B or Dk != D:
+        raise FdError(FD_ERR_INVALID_ARG, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise FdError(FD_ERR_UNSUPPORTED, "q, k and v must share one dtype")
+    if lens is not None:
+        if lens.dtype != torch.int32 or lens.shape != (B,):
+            raise FdError(FD_ERR_INVALID_ARG, "lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise FdError(FD_ERR_INVALID_ARG, "out must be [B, Hq, D]")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = decode_workspace_size(B, Hq, Hkv, D, Lmax, dt, n_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fd_decode_attn(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _opt_ptr(lens, "lens"),
+                              B, Hq, Hkv, D, Lmax, dt, int(n_splits), _dev_ptr(out, "out"), _dtype_code(out),
+                              _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def bifurcated_workspace_size(samples, q_heads, kv_heads, head_dim, ctx_len, dec_max_len, dtype):
+    n = _c_sz(0)
+    _check(load().fd_bifurcated_attn_workspace_size(samples, q_heads, kv_heads, head_dim, ctx_len,
+                                                    dec_max_len, dtype, ctypes.byref(n)))
+    return n.value
+
+
+def bifurcated_attn(q, k_ctx, v_ctx, k_dec, v_dec, dec_lens=None, out=None, out_dtype=None, scale=0.0,
+                    return_lse=False, workspace=None, stream=None):
+    """Bifurcated single-context batch-sampling attention (fd_bifurcated_attn).
+
+    q [S, Hq, D]; k_ctx, v_ctx [Hkv, Lc, D]; k_dec, v_dec [S, Hkv, Ldmax, D];
+    dec_lens int32 [S] (0..Ldmax) or None.
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k_ctx.dim() != 3 or k_dec.dim() != 4:
+        raise FdError(FD_ERR_INVALID_ARG, "expected q [S,Hq,D], k_ctx [Hkv,Lc,D], k_dec [S,Hkv,Ldmax,D]")
+    S, Hq, D = q.shape
+    Hkv, Lc, _ = k_ctx.shape
+    Ld = k_dec.shape[2]
+    if (v_ctx.shape != k_ctx.shape or v_dec.shape != k_dec.shape or k_ctx.shape[2] != D
+            or tuple(k_dec.shape) != (S, Hkv, Ld, D)):
+        raise FdError(FD_ERR_INVALID_ARG, "bifurcated shapes do not match")
+    dt = _dtype_code(q)
+    for t in (k_ctx, v_ctx, k_dec, v_dec):
+        if _dtype_code(t) != dt:
+            raise FdError(FD_ERR_UNSUPPORTED, "all inputs must share one dtype")
+    if dec_lens is not None and (dec_lens.dtype != torch.int32 or dec_lens.shape != (S,)):
+        raise FdError(FD_ERR_INVALID_ARG, "dec_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = bifurcated_workspace_size(S, Hq, Hkv, D, Lc, Ld, dt)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fd_bifurcated_attn(_dev_ptr(q, "q"), _dev_ptr(k_ctx, "k_ctx"), _dev_ptr(v_ctx, "v_ctx"),
+                                  _dev_ptr(k_dec, "k_dec"), _dev_ptr(v_dec, "v_dec"),
+                                  _opt_ptr(dec_lens, "dec_lens"), S, Hq, Hkv, D, Lc, Ld, dt,
+                                  _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"),
+                                  float(scale), _dev_ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def lse_combine(o_part, lse_part, out=None, out_dtype=None, return_lse=False, stream=None):
+    """fd_lse_combine: o_part [rows, P, D] fp32, lse_part [rows, P] fp32 -> out [rows, D]."""
+    torch = _torch()
+    lib = load()
+    rows, P, D = o_part.shape
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32 or tuple(lse_part.shape) != (rows, P):
+        raise FdError(FD_ERR_INVALID_ARG, "o_part [rows,P,D] and lse_part [rows,P] must be float32")
+    if out is None:
+        out = torch.empty((rows, D), dtype=out_dtype or torch.float32, device=o_part.device)
+    lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device) if return_lse else None
+    _check(lib.fd_lse_combine(_dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"), rows, P, D,
+                              _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"), _stream(stream)))
+    return (out, lse) if return_lse else out

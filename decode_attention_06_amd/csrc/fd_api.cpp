@@ -1,0 +1,361 @@
+// Host side of the C ABI declared in include/fd.h: argument validation,
+// split planning, workspace sizing and kernel launches.  Every check runs
+// before the first HIP call; no entry point allocates device memory or
+// synchronises a stream.
+#include "fd.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+#include "fd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fd_status fail(fd_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fd_status hip_fail(hipError_t e, const char* what) {
+    return fail(FD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int32_t kWgPerCu = 2;        // partial-kernel workgroups to keep per CU
+constexpr int64_t kMinChunk = 256;     // shortest piece worth a partial result
+constexpr int64_t kMaxLen = int64_t(1) << 30;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by decode and bifurcated calls.
+fd_status check_heads(int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype) {
+    if (Hq <= 0 || Hkv <= 0) return fail(FD_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(FD_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (D != 64 && D != 128) return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", D);
+    if (dtype != FD_F32 && dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    return FD_OK;
+}
+
+fd_status check_out_dtype(int32_t out_dtype) {
+    if (out_dtype != FD_F32 && out_dtype != FD_BF16)
+        return fail(FD_ERR_UNSUPPORTED, "out dtype %d not supported", out_dtype);
+    return FD_OK;
+}
+
+fd_status check_ptr(const void* p, size_t align, const char* name) {
+    if (!p) return fail(FD_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(FD_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    return FD_OK;
+}
+
+#define FD_TRY(expr)                  \
+    do {                              \
+        fd_status _s = (expr);        \
+        if (_s != FD_OK) return _s;   \
+    } while (0)
+
+std::mutex g_cu_mutex;
+std::vector<int32_t> g_cu_cache;
+
+struct PartialLayout {
+    size_t lse_bytes;   // [rows, parts] fp32, padded to kAlign
+    size_t o_bytes;     // [rows, parts, D] fp32
+    size_t total() const { return lse_bytes + o_bytes; }
+};
+
+PartialLayout partial_layout(int64_t rows, int64_t parts, int32_t D) {
+    PartialLayout L;
+    L.lse_bytes = align_up(size_t(rows * parts) * sizeof(float));
+    L.o_bytes = size_t(rows * parts * D) * sizeof(float);
+    return L;
+}
+
+float resolve_scale(float scale, int32_t D) {
+    return scale > 0.f ? scale : 1.0f / std::sqrt(float(D));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Pieces for the context and for the decode part of a bifurcated call.
+void plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld,
+                     int32_t dtype, int32_t n_cu, int32_t* pc, int32_t* pd) {
+    *pc = fd_plan_splits(S, Hq, Hkv, D, Lc, dtype, n_cu);
+    *pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_status_string(fd_status s) {
+    switch (s) {
+        case FD_OK: return "FD_OK";
+        case FD_ERR_INVALID_ARG: return "FD_ERR_INVALID_ARG";
+        case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
+        case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
+        case FD_ERR_HIP: return "FD_ERR_HIP";
+    }
+    return "FD_ERR_UNKNOWN";
+}
+
+const char* fd_last_error_message(void) { return g_err; }
+
+int32_t fd_version(void) { return 100; }
+
+int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t max_len, int32_t dtype, int32_t n_cu) {
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_len <= 0 ||
+        n_cu <= 0 || num_q_heads % num_kv_heads != 0 || (dtype != FD_F32 && dtype != FD_BF16))
+        return -1;
+    const int G = num_q_heads / num_kv_heads;
+    const int64_t units = int64_t(batch) * num_kv_heads * (G / fd::valu_rows_per_block(G));
+    const int64_t target = int64_t(n_cu) * kWgPerCu;
+    if (units >= target) return 1;
+    int64_t s = (target + units - 1) / units;
+    const int64_t by_len = std::max<int64_t>(1, max_len / kMinChunk);
+    s = std::min<int64_t>(s, by_len);
+    s = std::min<int64_t>(s, FD_MAX_SPLITS);
+    return int32_t(std::max<int64_t>(s, 1));
+}
+
+fd_status fd_device_cu_count(int32_t* n_cu) {
+    if (!n_cu) return fail(FD_ERR_INVALID_ARG, "n_cu is NULL");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (dev >= int(g_cu_cache.size())) g_cu_cache.resize(dev + 1, 0);
+    if (g_cu_cache[dev] == 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+        if (cus <= 0) return fail(FD_ERR_HIP, "device reports %d compute units", cus);
+        g_cu_cache[dev] = cus;
+    }
+    *n_cu = g_cu_cache[dev];
+    return FD_OK;
+}
+
+static fd_status check_decode_shapes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
+                                     int32_t dtype, int32_t n_splits) {
+    if (B <= 0) return fail(FD_ERR_INVALID_ARG, "batch must be positive (got %d)", B);
+    if (Lmax <= 0 || Lmax > kMaxLen)
+        return fail(FD_ERR_INVALID_ARG, "max_len %lld outside [1, 2^30]", (long long)Lmax);
+    if (n_splits > FD_MAX_SPLITS)
+        return fail(FD_ERR_INVALID_ARG, "n_splits %d above FD_MAX_SPLITS", n_splits);
+    return check_heads(Hq, Hkv, D, dtype);
+}
+
+static fd_status resolve_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
+                                int32_t dtype, int32_t n_splits, int32_t* out) {
+    if (n_splits > 0) {
+        *out = n_splits;
+        return FD_OK;
+    }
+    int32_t cus = 0;
+    FD_TRY(fd_device_cu_count(&cus));
+    *out = fd_plan_splits(B, Hq, Hkv, D, Lmax, dtype, cus);
+    return FD_OK;
+}
+
+fd_status fd_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
+                                        int32_t dtype, int32_t n_splits, size_t* bytes) {
+    if (!bytes) return fail(FD_ERR_INVALID_ARG, "bytes is NULL");
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    int32_t ns = 0;
+    FD_TRY(resolve_splits(B, Hq, Hkv, D, Lmax, dtype, n_splits, &ns));
+    *bytes = (ns == 1) ? 0 : partial_layout(int64_t(B) * Hq, ns, D).total();
+    return FD_OK;
+}
+
+fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int32_t* lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype,
+                         int32_t n_splits, void* out, int32_t out_dtype, float* lse_out, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    FD_TRY(check_out_dtype(out_dtype));
+    FD_TRY(check_ptr(q, 16, "q"));
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    FD_TRY(check_ptr(out, 16, "out"));
+    if (lens && !aligned(lens, 4)) return fail(FD_ERR_INVALID_ARG, "lens is not 4-byte aligned");
+    if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
+
+    int32_t ns = 0;
+    FD_TRY(resolve_splits(B, Hq, Hkv, D, Lmax, dtype, n_splits, &ns));
+    const int64_t rows = int64_t(B) * Hq;
+    const PartialLayout L = partial_layout(rows, ns, D);
+    if (ns > 1) {
+        if (!workspace) return fail(FD_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", L.total());
+        if (!aligned(workspace, 16)) return fail(FD_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+        if (workspace_bytes < L.total())
+            return fail(FD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total());
+    }
+
+    const int G = Hq / Hkv;
+    const int GB = fd::valu_rows_per_block(G);
+    fd::PartialParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lens = lens;
+    p.out = out;
+    p.lse_out = lse_out;
+    p.Lmax = Lmax;
+    p.kv_stride_h = Lmax * D;
+    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.n_splits = ns;
+    p.row_blocks = G / GB;
+    p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+    p.out_bf16 = out_dtype == FD_BF16;
+    p.direct = ns == 1;
+    float* lse_part = nullptr;
+    float* o_part = nullptr;
+    if (ns > 1) {
+        lse_part = static_cast<float*>(workspace);
+        o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_bytes);
+        p.o_part = o_part;
+        p.lse_part = lse_part;
+        p.part_stride = ns;
+        p.part_offset = 0;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    if (e != hipSuccess) return hip_fail(e, "split-KV partial kernel launch");
+    if (ns > 1) {
+        e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), ns, D, out, p.out_bf16, lse_out, s);
+        if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
+    }
+    return FD_OK;
+}
+
+static fd_status check_bifurcated_shapes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc,
+                                         int64_t Ld, int32_t dtype) {
+    if (S <= 0) return fail(FD_ERR_INVALID_ARG, "samples must be positive (got %d)", S);
+    if (Lc <= 0 || Lc > kMaxLen)
+        return fail(FD_ERR_INVALID_ARG, "ctx_len %lld outside [1, 2^30]", (long long)Lc);
+    if (Ld <= 0 || Ld > kMaxLen)
+        return fail(FD_ERR_INVALID_ARG, "dec_max_len %lld outside [1, 2^30]", (long long)Ld);
+    return check_heads(Hq, Hkv, D, dtype);
+}
+
+fd_status fd_bifurcated_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc,
+                                            int64_t Ld, int32_t dtype, size_t* bytes) {
+    if (!bytes) return fail(FD_ERR_INVALID_ARG, "bytes is NULL");
+    FD_TRY(check_bifurcated_shapes(S, Hq, Hkv, D, Lc, Ld, dtype));
+    int32_t cus = 0;
+    FD_TRY(fd_device_cu_count(&cus));
+    int32_t pc = 0, pd = 0;
+    plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus, &pc, &pd);
+    *bytes = partial_layout(int64_t(S) * Hq, pc + pd, D).total();
+    return FD_OK;
+}
+
+fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx, const void* k_dec,
+                             const void* v_dec, const int32_t* dec_lens, int32_t S, int32_t Hq,
+                             int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld, int32_t dtype, void* out,
+                             int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    FD_TRY(check_bifurcated_shapes(S, Hq, Hkv, D, Lc, Ld, dtype));
+    FD_TRY(check_out_dtype(out_dtype));
+    FD_TRY(check_ptr(q, 16, "q"));
+    FD_TRY(check_ptr(k_ctx, 16, "k_ctx"));
+    FD_TRY(check_ptr(v_ctx, 16, "v_ctx"));
+    FD_TRY(check_ptr(k_dec, 16, "k_dec"));
+    FD_TRY(check_ptr(v_dec, 16, "v_dec"));
+    FD_TRY(check_ptr(out, 16, "out"));
+    if (dec_lens && !aligned(dec_lens, 4)) return fail(FD_ERR_INVALID_ARG, "dec_lens is not 4-byte aligned");
+    if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
+    if (!workspace) return fail(FD_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(FD_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+
+    int32_t cus = 0;
+    FD_TRY(fd_device_cu_count(&cus));
+    int32_t pc = 0, pd = 0;
+    plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus, &pc, &pd);
+    const int32_t P = pc + pd;
+    const int64_t rows = int64_t(S) * Hq;
+    const PartialLayout L = partial_layout(rows, P, D);
+    if (workspace_bytes < L.total())
+        return fail(FD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total());
+    float* lse_part = static_cast<float*>(workspace);
+    float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_bytes);
+
+    const int G = Hq / Hkv;
+    const int GB = fd::valu_rows_per_block(G);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // Context part: every sample reads the same [Hkv, Lc, D] rows (batch
+    // stride 0); all Lc rows are valid.
+    fd::PartialParams p{};
+    p.q = q;
+    p.k = k_ctx;
+    p.v = v_ctx;
+    p.lens = nullptr;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.Lmax = Lc;
+    p.kv_stride_b = 0;
+    p.kv_stride_h = Lc * D;
+    p.B = S;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.n_splits = pc;
+    p.row_blocks = G / GB;
+    p.part_stride = P;
+    p.part_offset = 0;
+    p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+    p.direct = 0;
+    hipError_t e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+
+    // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
+    p.k = k_dec;
+    p.v = v_dec;
+    p.lens = dec_lens;
+    p.Lmax = Ld;
+    p.kv_stride_h = Ld * D;
+    p.kv_stride_b = int64_t(Hkv) * Ld * D;
+    p.n_splits = pd;
+    p.part_offset = pc;
+    e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    if (e != hipSuccess) return hip_fail(e, "bifurcated decode kernel launch");
+
+    e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), P, D, out, out_dtype == FD_BF16, lse_out, s);
+    if (e != hipSuccess) return hip_fail(e, "bifurcated combine kernel launch");
+    return FD_OK;
+}
+
+fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t rows, int32_t n_parts,
+                         int32_t D, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+    if (rows <= 0 || n_parts <= 0) return fail(FD_ERR_INVALID_ARG, "rows and n_parts must be positive");
+    if (D <= 0 || D > 512) return fail(FD_ERR_UNSUPPORTED, "head_dim %d outside [1, 512]", D);
+    FD_TRY(check_out_dtype(out_dtype));
+    FD_TRY(check_ptr(o_part, 4, "o_part"));
+    FD_TRY(check_ptr(lse_part, 4, "lse_part"));
+    FD_TRY(check_ptr(out, out_dtype == FD_BF16 ? 2 : 4, "out"));
+    if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
+    hipError_t e = fd::launch_lse_combine(o_part, lse_part, rows, n_parts, D, out, out_dtype == FD_BF16,
+                                          lse_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
+    return FD_OK;
+}
+
+}  // extern "C"

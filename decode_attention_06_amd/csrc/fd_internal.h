@@ -1,0 +1,49 @@
+// Internal interface between the host layer (fd_api.cpp) and the kernels
+// (fd_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fd {
+
+// One launch of the split-KV partial kernel.  A work unit is
+// (sequence b, KV head, block of query rows, piece); every unit streams its
+// piece of the KV rows once and keeps a running max / running sum per query
+// row (the online softmax).
+struct PartialParams {
+    const void* q;          // [B, Hq, D]
+    const void* k;          // element (b, kvh, t, d) at b*kv_stride_b + kvh*kv_stride_h + t*D + d
+    const void* v;
+    const int32_t* lens;    // [B] valid rows per sequence, or nullptr = Lmax
+    void* out;              // direct mode: final output [B, Hq, D]
+    float* lse_out;         // direct mode: [B, Hq] natural-log lse, or nullptr
+    float* o_part;          // partial mode: [B*Hq, part_stride, D]
+    float* lse_part;        // partial mode: [B*Hq, part_stride]
+    int64_t Lmax;           // rows available per (b, kv head)
+    int64_t kv_stride_b;    // elements; 0 makes every sequence read the same KV
+    int64_t kv_stride_h;    // elements
+    int32_t B, Hq, Hkv;
+    int32_t n_splits;       // pieces per sequence in this launch
+    int32_t row_blocks;     // query-row blocks per KV head (G / rows per block)
+    int32_t part_stride;    // pieces per output row in o_part / lse_part
+    int32_t part_offset;    // first piece slot written by this launch
+    float scale_log2;       // softmax scale * log2(e)
+    int32_t out_bf16;       // direct mode output dtype
+    int32_t direct;         // 1: n_splits == 1, write the final output
+};
+
+// Query rows handled by one work unit of the vector-ALU partial kernel for a
+// GQA group of G query heads: the largest of 8, 4, 2, 1 that divides G.
+inline int valu_rows_per_block(int G) {
+    return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
+
+hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, int rows_per_block,
+                               hipStream_t stream);
+
+hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
+                              int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
+                              float* lse_out, hipStream_t stream);
+
+}  // namespace fd

@@ -1,0 +1,389 @@
+// Split-KV decode-attention kernels for gfx950 (CDNA4, wave64).
+//
+// Method: [FD] "¿Qué es Flash-Decoding y cuándo acelera los LLMs?"
+// (slavadubrov.com), section "Por qué la decodificación necesita otra
+// planificación": the cached history of each sequence is cut into pieces
+// that run as independent work units; each produces a normalised partial
+// output and its log-sum-exp, and a reduction renormalises them.  Inside a
+// piece the scores never leave the chip: [FA] "In che modo Flash Attention
+// riduce il traffico di memoria durante l'inferenza locale?"
+// (shop.zimaspace.com), sections on tiling, on the online softmax (running
+// max and running sum carried across tiles) and on kernel fusion.
+//
+// Vector-ALU kernel layout (one 64-lane wave):
+//   Each KV row (one token, D elements) is split into 16-byte vectors; LPR
+//   consecutive lanes hold one row, so a wave-wide load covers RPW = 64/LPR
+//   consecutive rows = 1 KiB of contiguous cache.  A lane keeps the query
+//   elements matching its 16-byte slice in registers, forms partial dot
+//   products, and a DPP butterfly inside each LPR-lane row group completes
+//   the score.  Each row group runs its own online softmax over the tokens it
+//   sees (no cross-group max per tile); groups and waves are merged once per
+//   piece.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+namespace {
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Unpack one 16-byte vector of storage type T into floats.
+template <typename T>
+struct Vec16;
+
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(const uint4& r, float* f) {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+};
+
+template <>
+struct Vec16<uint16_t> {  // bf16 bits
+    static constexpr int N = 8;
+    __device__ static void unpack(const uint4& r, float* f) {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+        f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+        f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of LPR lanes; every lane of the group ends
+// with the same bits (each step adds a pair in both orders, and float
+// addition commutes).  DPP: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror; a 32-lane group adds one cross-row swap.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (LPR >= 2) x += dpp<0xB1>(x);
+    if constexpr (LPR >= 4) x += dpp<0x4E>(x);
+    if constexpr (LPR >= 8) x += dpp<0x141>(x);
+    if constexpr (LPR >= 16) x += dpp<0x140>(x);
+    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v, int bf16) {
+    if (bf16)
+        static_cast<uint16_t*>(out)[idx] = to_bf16(v);
+    else
+        static_cast<float*>(out)[idx] = v;
+}
+
+// Merge running state (m2, l2) into (m, l); returns the weights applied to
+// the old and the incoming accumulators.  -inf marks "no row seen yet".
+__device__ __forceinline__ void merge_weights(float m, float m2, float& mn, float& w1, float& w2) {
+    mn = fmaxf(m, m2);
+    const float ref = (mn == -INFINITY) ? 0.f : mn;
+    w1 = fast_exp2(m - ref);
+    w2 = fast_exp2(m2 - ref);
+}
+
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p) {
+    constexpr int EPL = Vec16<T>::N;     // elements per lane per row
+    constexpr int LPR = D / EPL;         // lanes per KV row
+    constexpr int RPW = 64 / LPR;        // KV rows per wave-wide load
+    constexpr int U = (GB <= 2) ? 8 : 4; // loads in flight per lane, per K and V
+    constexpr int NW = 4;                // waves per workgroup
+    constexpr int WAVE_TOK = RPW * U;
+    constexpr int WG_TOK = NW * WAVE_TOK;
+    static_assert(LPR * RPW == 64, "row groups must tile the wave");
+
+    __shared__ float s_acc[NW][GB][D];
+    __shared__ float s_m[NW][GB];
+    __shared__ float s_l[NW][GB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane / LPR, c = lane % LPR;
+
+    int idx = blockIdx.x;
+    const int split = idx % p.n_splits;
+    idx /= p.n_splits;
+    const int rb = idx % p.row_blocks;
+    idx /= p.row_blocks;
+    const int kvh = idx % p.Hkv;
+    const int b = idx / p.Hkv;
+    const int h0 = kvh * (GB * p.row_blocks) + rb * GB;
+
+    // Valid rows of this sequence and this unit's piece [t0, t1).  The piece
+    // length is ceil(n / n_splits) rounded up to 16 rows.
+    int n = p.lens ? p.lens[b] : (int)p.Lmax;
+    n = max(0, min(n, (int)p.Lmax));
+    const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
+    const int t0 = (int)min((int64_t)split * chunk, (int64_t)n);
+    const int t1 = min(t0 + chunk, n);
+
+    // Query slice of this lane, pre-multiplied by scale*log2(e) so that
+    // exp2 of a score difference is the softmax weight ratio.
+    float qf[GB][EPL];
+#pragma unroll
+    for (int g = 0; g < GB; ++g) {
+        const T* qp = static_cast<const T*>(p.q) + ((int64_t)b * p.Hq + h0 + g) * D + c * EPL;
+        Vec16<T>::unpack(*reinterpret_cast<const uint4*>(qp), qf[g]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
+    }
+
+    const T* kb = static_cast<const T*>(p.k) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + c * EPL;
+    const T* vb = static_cast<const T*>(p.v) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + c * EPL;
+
+    float m[GB], l[GB], acc[GB][EPL];
+#pragma unroll
+    for (int g = 0; g < GB; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+
+    for (int tb = t0 + wave * WAVE_TOK; tb < t1; tb += WG_TOK) {
+        const bool full = tb + WAVE_TOK <= t1;
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u * RPW + r;
+            if (full || t < t1) {
+                kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
+                vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
+            } else {
+                kr[u] = make_uint4(0, 0, 0, 0);
+                vr[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        // Scores (log2 domain).  All lanes take part in the DPP sums.
+        float s[U][GB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[EPL];
+            Vec16<T>::unpack(kr[u], kf);
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kf[e], d);
+                s[u][g] = group_sum<LPR>(d);
+            }
+        }
+        if (!full) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (tb + u * RPW + r >= t1)
+#pragma unroll
+                    for (int g = 0; g < GB; ++g) s[u][g] = -INFINITY;
+        }
+
+        // Online softmax update, one rescale per tile.
+        float pr[U][GB];
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+            float mt = s[0][g];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+            const float mn = fmaxf(m[g], mt);
+            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m[g] - ref);
+            float lsum = l[g] * alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                pr[u][g] = fast_exp2(s[u][g] - ref);
+                lsum += pr[u][g];
+            }
+            l[g] = lsum;
+            m[g] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            Vec16<T>::unpack(vr[u], vf);
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[u][g], vf[e], acc[g][e]);
+        }
+    }
+
+    // Merge the RPW row groups of the wave (butterfly across lane offsets
+    // LPR, 2*LPR, ...).  Afterwards group 0 holds the wave's state.
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+            const float m2 = __shfl_xor(m[g], off);
+            const float l2 = __shfl_xor(l[g], off);
+            float mn, w1, w2;
+            merge_weights(m[g], m2, mn, w1, w2);
+            l[g] = l[g] * w1 + l2 * w2;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * w1 + __shfl_xor(acc[g][e], off) * w2;
+            m[g] = mn;
+        }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s_acc[wave][g][c * EPL + e] = acc[g][e];
+            if (c == 0) {
+                s_m[wave][g] = m[g];
+                s_l[wave][g] = l[g];
+            }
+        }
+    }
+    __syncthreads();
+
+    // Merge the waves (fixed order) and write this piece's result.
+    for (int i = tid; i < GB * D; i += NW * 64) {
+        const int g = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+        float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float a = fast_exp2(s_m[w][g] - M);
+                L = fmaf(s_l[w][g], a, L);
+                A = fmaf(s_acc[w][g][d], a, A);
+            }
+        }
+        const float o = (L > 0.f) ? A / L : 0.f;
+        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        const int64_t row = (int64_t)b * p.Hq + h0 + g;
+        if (p.direct) {
+            store_out(p.out, row * D + d, o, p.out_bf16);
+            if (d == 0 && p.lse_out) p.lse_out[row] = lse;
+        } else {
+            const int64_t slot = row * p.part_stride + p.part_offset + split;
+            p.o_part[slot * D + d] = o;
+            if (d == 0) p.lse_part[slot] = lse;
+        }
+    }
+}
+
+// LSE combine: one workgroup per (row, 32-wide slice of D).  Thread
+// (pg, dl) sums pieces pg, pg+8, ... for column slice*32 + dl; the eight
+// partial sums are then added in a fixed order.
+constexpr int CMB_SLICE = 32;
+constexpr int CMB_GROUPS = 8;
+
+__global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restrict__ o_part,
+                                                          const float* __restrict__ lse_part,
+                                                          int32_t n_parts, int32_t D, void* out,
+                                                          int32_t out_bf16, float* lse_out) {
+    __shared__ float s_red[256];
+    __shared__ float s_acc[CMB_GROUPS][CMB_SLICE];
+    __shared__ float s_w[CMB_GROUPS];
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int slice = blockIdx.y;
+    const float* lrow = lse_part + row * n_parts;
+
+    // Row maximum of the piece lse values.
+    float M = -INFINITY;
+    for (int i = tid; i < n_parts; i += 256) M = fmaxf(M, lrow[i]);
+    s_red[tid] = M;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) s_red[tid] = fmaxf(s_red[tid], s_red[tid + s]);
+        __syncthreads();
+    }
+    M = s_red[0];
+
+    const int dl = tid % CMB_SLICE, pg = tid / CMB_SLICE;
+    const int d = slice * CMB_SLICE + dl;
+    float A = 0.f, W = 0.f;
+    if (M != -INFINITY) {
+        for (int i = pg; i < n_parts; i += CMB_GROUPS) {
+            const float li = lrow[i];
+            const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2e);
+            W += w;
+            if (d < D) A = fmaf(w, o_part[(row * n_parts + i) * D + d], A);
+        }
+    }
+    s_acc[pg][dl] = A;
+    if (dl == 0) s_w[pg] = W;
+    __syncthreads();
+    if (pg == 0 && d < D) {
+        float a = 0.f, z = 0.f;
+#pragma unroll
+        for (int g = 0; g < CMB_GROUPS; ++g) {
+            a += s_acc[g][dl];
+            z += s_w[g];
+        }
+        const float o = (z > 0.f) ? a / z : 0.f;
+        store_out(out, row * D + d, o, out_bf16);
+        if (d == 0 && lse_out) lse_out[row] = (z > 0.f) ? M + logf(z) : -INFINITY;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_valu_rows(const PartialParams& p, int rows_per_block, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks * p.n_splits));
+    const dim3 block(256);
+    switch (rows_per_block) {
+        case 1: hipLaunchKernelGGL((partial_valu_kernel<T, D, 1>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((partial_valu_kernel<T, D, 2>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((partial_valu_kernel<T, D, 4>), grid, block, 0, stream, p); break;
+        case 8: hipLaunchKernelGGL((partial_valu_kernel<T, D, 8>), grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, int rows_per_block,
+                               hipStream_t stream) {
+    if (dtype == 0) {
+        if (head_dim == 64) return launch_valu_rows<float, 64>(p, rows_per_block, stream);
+        if (head_dim == 128) return launch_valu_rows<float, 128>(p, rows_per_block, stream);
+    } else {
+        if (head_dim == 64) return launch_valu_rows<uint16_t, 64>(p, rows_per_block, stream);
+        if (head_dim == 128) return launch_valu_rows<uint16_t, 128>(p, rows_per_block, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
+                              int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
+                              float* lse_out, hipStream_t stream) {
+    const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
+    hipLaunchKernelGGL(lse_combine_kernel, grid, dim3(256), 0, stream, o_part, lse_part, n_parts,
+                       head_dim, out, out_bf16, lse_out);
+    return hipGetLastError();
+}
+
+}  // namespace fd

@@ -1,0 +1,202 @@
+/*
+ * fd.h - C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * Exact single-query (decode-step) attention over a long KV cache, built as
+ * split-KV partials plus a log-sum-exp combine, and a bifurcated variant
+ * for many samples that share one context.
+ *
+ * Sources (pages cited by title and section):
+ *  [FD] "¿Qué es Flash-Decoding y cuándo acelera los LLMs?" (slavadubrov.com),
+ *       section "Por qué la decodificación necesita otra planificación":
+ *       decode attention is parallelised along the cached sequence; every
+ *       piece produces a partial output and a log-sum-exp; a reduction
+ *       renormalises them into the full-history result.
+ *  [FA] "In che modo Flash Attention riduce il traffico di memoria durante
+ *       l'inferenza locale?" (shop.zimaspace.com), sections on tiling, on
+ *       the online softmax and on kernel fusion; and "Il supporto hardware e
+ *       la forma dei dati determinano l'uso del percorso rapido": fast paths
+ *       are specialised by head size, dtype and shape.
+ *  [BA] "Effiziente Verarbeitung und Analyse von Inhalten durch bifurkierte
+ *       Aufmerksamkeit für Single-Context-Batch-Sampling" (linnk.ai),
+ *       sections "Tiivistelmä" and "Tilastot": attention over a shared
+ *       context KV plus per-sample decode KV, exact, with the context KV
+ *       read once; GQA/MQA heads share KV heads.
+ *
+ * Conventions shared by every entry point
+ *  - Every data pointer is a device pointer owned by the caller.  The
+ *    library never allocates or frees device memory and never synchronises
+ *    the stream; work is enqueued on `stream` (a hipStream_t, NULL = the
+ *    default stream) and faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Tensors are dense and row-major, last index fastest:
+ *        q    [B, Hq, D]            (bifurcated: [S, Hq, D])
+ *        k, v [B, Hkv, Lmax, D]     (context: [Hkv, Lc, D];
+ *                                    decode: [S, Hkv, Ldmax, D])
+ *        out  [B, Hq, D]
+ *    q, k, v and out must be 16-byte aligned; lens, lse buffers 4-byte.
+ *  - Query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ *  - Supported: q/k/v dtype FD_F32 or FD_BF16 (all three the same), out
+ *    dtype FD_F32 or FD_BF16 (bf16 is rounded to nearest even), head_dim
+ *    64 or 128, Hq a multiple of Hkv.  Anything else returns
+ *    FD_ERR_UNSUPPORTED; there is no silent fallback.
+ *  - Every shape, pointer, alignment and workspace check runs before the
+ *    first HIP call; a failing check returns its status and leaves the
+ *    stream untouched.  Device-resident lengths cannot be checked without a
+ *    synchronisation and are preconditions.
+ *  - Errors are returned as fd_status; fd_last_error_message() gives a
+ *    thread-local description of the most recent failure.  No entry point
+ *    aborts or throws.
+ *  - scale <= 0 selects 1/sqrt(head_dim).  lse values are natural-log
+ *    log-sum-exps of the scaled scores.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size          */
+    FD_ERR_UNSUPPORTED = 2,   /* valid request the kernels do not implement */
+    FD_ERR_WORKSPACE = 3,     /* workspace missing or too small             */
+    FD_ERR_HIP = 4            /* the HIP runtime reported an error          */
+} fd_status;
+
+typedef enum fd_dtype {
+    FD_F32 = 0,
+    FD_BF16 = 1
+} fd_dtype;
+
+/* Largest split count accepted (per sequence for decode; context plus
+ * decode pieces for the bifurcated call). */
+#define FD_MAX_SPLITS 4096
+
+/* Human-readable name of a status code (static string). */
+const char* fd_status_string(fd_status status);
+
+/* Thread-local text describing the last non-OK status returned on this
+ * thread ("" if none). */
+const char* fd_last_error_message(void);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int32_t fd_version(void);
+
+/*
+ * fd_plan_splits - split count for one decode call ([FD] section "Por qué
+ * la decodificación necesita otra planificación": split only when batch x
+ * heads alone leaves the GPU short of independent work, and not so far that
+ * the pieces become too short to pay for the partial results).
+ *
+ * Pure host function; reads no device state.  n_cu is the number of
+ * compute units to fill (256 on MI355X).  Returns a count in
+ * [1, FD_MAX_SPLITS], or -1 for invalid arguments.  It depends only on
+ * shapes, never on the device-resident lengths.
+ */
+int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int64_t max_len, int32_t dtype, int32_t n_cu);
+
+/*
+ * fd_device_cu_count - compute units of the current HIP device (cached per
+ * device).  Returns FD_ERR_HIP when no device is usable.
+ */
+fd_status fd_device_cu_count(int32_t* n_cu);
+
+/*
+ * fd_decode_attn_workspace_size - bytes of device workspace fd_decode_attn
+ * needs for these shapes and this n_splits (<= 0: the planner's count for
+ * the current device, which needs a visible device).  The workspace holds
+ * the per-piece partial outputs [B, Hq, n_splits, D] fp32 and their lse
+ * [B, Hq, n_splits] fp32; it is 0 bytes when one piece suffices.
+ */
+fd_status fd_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int64_t max_len, int32_t dtype,
+                                        int32_t n_splits, size_t* bytes);
+
+/*
+ * fd_decode_attn - split-KV decode attention ([FD] "Por qué la
+ * decodificación necesita otra planificación"; [FA] online softmax and
+ * fusion; [BA] "Tilastot" for the KV-head sharing).
+ *
+ *   q        [B, Hq, D]        one query position per sequence
+ *   k, v     [B, Hkv, Lmax, D] KV cache; row t of sequence b is valid for
+ *                              t < lens[b]; other rows are never read
+ *   lens     device int32 [B], each in [1, Lmax]; NULL = all Lmax
+ *   n_splits pieces per sequence, <= 0 = fd_plan_splits() for the current
+ *            device; a forced count above what the length needs yields
+ *            empty pieces, which are legal
+ *   out      [B, Hq, D] in out_dtype
+ *   lse_out  device fp32 [B, Hq] (natural log) or NULL
+ *   scale    softmax temperature; <= 0 selects 1/sqrt(D)
+ *   workspace, workspace_bytes: device scratch of at least
+ *            fd_decode_attn_workspace_size() bytes (may be NULL when that
+ *            size is 0); 256-byte alignment recommended
+ *   stream   hipStream_t or NULL
+ *
+ * The result for fixed inputs and a fixed n_splits is bitwise repeatable
+ * (fixed reduction order, no float atomics).
+ */
+fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                         int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int64_t max_len, int32_t dtype,
+                         int32_t n_splits, void* out, int32_t out_dtype, float* lse_out,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fd_bifurcated_attn_workspace_size - bytes of workspace fd_bifurcated_attn
+ * needs: partials of every context piece and every decode piece,
+ * [S, Hq, P, D] fp32 plus [S, Hq, P] fp32.
+ */
+fd_status fd_bifurcated_attn_workspace_size(int32_t samples, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int64_t ctx_len, int64_t dec_max_len,
+                                            int32_t dtype, size_t* bytes);
+
+/*
+ * fd_bifurcated_attn - single-context batch-sampling attention ([BA]
+ * "Tiivistelmä"): S samples share one context KV; each also has its own
+ * decode KV.  The result equals standard attention of every sample over
+ * [context rows ; its own valid decode rows].
+ *
+ *   q             [S, Hq, D]
+ *   k_ctx, v_ctx  [Hkv, Lc, D], Lc >= 1 (all rows valid)
+ *   k_dec, v_dec  [S, Hkv, Ldmax, D], Ldmax >= 1
+ *   dec_lens      device int32 [S], each in [0, Ldmax]; NULL = all Ldmax
+ *   out, lse_out, scale, workspace, stream: as in fd_decode_attn
+ */
+fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx,
+                             const void* k_dec, const void* v_dec, const int32_t* dec_lens,
+                             int32_t samples, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int64_t ctx_len, int64_t dec_max_len,
+                             int32_t dtype, void* out, int32_t out_dtype, float* lse_out,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * fd_lse_combine - the reduction of [FD] on its own: merges per-piece
+ * normalised outputs and their natural-log lse into the full result.
+ *
+ *   o_part    device fp32 [rows, n_parts, D]
+ *   lse_part  device fp32 [rows, n_parts]; -inf marks an empty piece, which
+ *             carries zero weight; every row needs one finite entry (a row
+ *             with none gets out = 0 and lse = -inf)
+ *   head_dim  D, any value in [1, 512] (the combine does not need 64/128)
+ *   out       [rows, D] in out_dtype;  lse_out fp32 [rows] or NULL
+ *
+ * Piece weights are exp(lse_i - max_j lse_j); out = sum w_i O_i / sum w_i;
+ * lse = max_j lse_j + ln(sum w_i).  Fixed summation order.
+ */
+fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
+                         int32_t n_parts, int32_t head_dim, void* out, int32_t out_dtype,
+                         float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

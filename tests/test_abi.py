@@ -1,0 +1,181 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+plans splits, and rejects bad arguments before any HIP call.
+
+Nothing here launches a kernel; the pointers passed are fake device
+addresses that the host checks never dereference.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_06_amd as fd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+FAKE = 0x10000          # 16-byte aligned non-null "device" address
+MISALIGNED = 0x10002
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in fd.h but not exported"
+        assert name in fd.SIGNATURES, f"{name} has no ctypes signature in the binding"
+
+
+def test_status_strings(lib):
+    assert fd.status_name(fd.FD_OK) == "FD_OK"
+    assert fd.status_name(fd.FD_ERR_WORKSPACE) == "FD_ERR_WORKSPACE"
+    assert lib.fd_version() >= 100
+
+
+# ---------------------------------------------------------------- planner
+
+def test_plan_invalid_arguments():
+    assert fd.plan_splits(0, 4, 4, 64, 512, fd.FD_F32, 256) == -1
+    assert fd.plan_splits(1, 6, 4, 64, 512, fd.FD_F32, 256) == -1      # Hq % Hkv
+    assert fd.plan_splits(1, 4, 4, 64, 0, fd.FD_F32, 256) == -1
+    assert fd.plan_splits(1, 4, 4, 64, 512, 7, 256) == -1
+    assert fd.plan_splits(1, 4, 4, 64, 512, fd.FD_F32, 0) == -1
+
+
+def test_plan_full_gpu_needs_no_split():
+    # batch x heads already covers every CU twice over: one piece
+    assert fd.plan_splits(16, 32, 32, 128, 65536, fd.FD_BF16, 256) == 1
+    assert fd.plan_splits(64, 8, 8, 128, 1 << 20, fd.FD_BF16, 256) == 1
+
+
+def test_plan_long_single_sequence_splits_a_lot():
+    s = fd.plan_splits(1, 16, 2, 128, 65536, fd.FD_BF16, 256)
+    assert 128 <= s <= 512
+
+
+def test_plan_short_history_limits_splitting():
+    # pieces are never planned shorter than the minimum chunk
+    assert fd.plan_splits(1, 32, 32, 128, 512, fd.FD_BF16, 256) <= 2
+    assert fd.plan_splits(1, 4, 4, 64, 100, fd.FD_F32, 256) == 1
+
+
+@pytest.mark.parametrize("L", [512, 2048, 8192, 32768, 65536, 1 << 20])
+def test_plan_monotone_in_work_units(L):
+    prev = None
+    for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        s = fd.plan_splits(B, 32, 32, 128, L, fd.FD_BF16, 256)
+        assert 1 <= s <= fd.FD_MAX_SPLITS
+        if prev is not None:
+            assert s <= prev, "more independent units never asks for more pieces"
+        prev = s
+
+
+def test_plan_monotone_in_length():
+    prev = 0
+    for L in (256, 1024, 4096, 16384, 65536, 1 << 18):
+        s = fd.plan_splits(1, 16, 2, 128, L, fd.FD_BF16, 256)
+        assert s >= prev
+        prev = s
+
+
+# ---------------------------------------------------------- argument checks
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=None, B=1, Hq=4, Hkv=4, D=64, L=512, dtype=fd.FD_F32,
+             n_splits=4, out=FAKE, out_dtype=fd.FD_F32, lse=None, scale=0.0, ws=FAKE, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.fd_decode_attn(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["L"],
+                              a["dtype"], a["n_splits"], a["out"], a["out_dtype"], a["lse"], a["scale"],
+                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(k=None), fd.FD_ERR_INVALID_ARG),
+    (dict(v=None), fd.FD_ERR_INVALID_ARG),
+    (dict(out=None), fd.FD_ERR_INVALID_ARG),
+    (dict(q=MISALIGNED), fd.FD_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), fd.FD_ERR_INVALID_ARG),
+    (dict(lens=0x10001), fd.FD_ERR_INVALID_ARG),
+    (dict(B=0), fd.FD_ERR_INVALID_ARG),
+    (dict(L=0), fd.FD_ERR_INVALID_ARG),
+    (dict(L=(1 << 30) + 1), fd.FD_ERR_INVALID_ARG),
+    (dict(Hq=6), fd.FD_ERR_UNSUPPORTED),
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(D=256), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=5), fd.FD_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), fd.FD_ERR_UNSUPPORTED),
+    (dict(n_splits=fd.FD_MAX_SPLITS + 1), fd.FD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=None), fd.FD_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fd.FD_ERR_WORKSPACE),
+    (dict(ws=0x10008, ws_bytes=1 << 20), fd.FD_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_any_hip_call(lib, kw, status):
+    st = _decode(lib, **kw)
+    assert st == status, (st, fd.load().fd_last_error_message())
+    assert lib.fd_last_error_message().decode()
+
+
+def test_bifurcated_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=FAKE, vd=FAKE, dl=None, S=4, Hq=8, Hkv=2, D=128, Lc=64, Ld=8,
+                 dtype=fd.FD_BF16, out=FAKE, odt=fd.FD_BF16, lse=None, scale=0.0, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return lib.fd_bifurcated_attn(a["q"], a["kc"], a["vc"], a["kd"], a["vd"], a["dl"], a["S"], a["Hq"],
+                                      a["Hkv"], a["D"], a["Lc"], a["Ld"], a["dtype"], a["out"], a["odt"],
+                                      a["lse"], a["scale"], a["ws"], a["wsb"], None)
+    assert call(kc=None) == fd.FD_ERR_INVALID_ARG
+    assert call(vd=MISALIGNED) == fd.FD_ERR_INVALID_ARG
+    assert call(S=0) == fd.FD_ERR_INVALID_ARG
+    assert call(Lc=0) == fd.FD_ERR_INVALID_ARG
+    assert call(Ld=0) == fd.FD_ERR_INVALID_ARG
+    assert call(Hkv=3) == fd.FD_ERR_UNSUPPORTED
+    assert call(D=80) == fd.FD_ERR_UNSUPPORTED
+    assert call(ws=None) == fd.FD_ERR_WORKSPACE
+    assert call(dl=0x10003) == fd.FD_ERR_INVALID_ARG
+
+
+def test_combine_rejects_bad_arguments(lib):
+    assert lib.fd_lse_combine(FAKE, FAKE, 0, 4, 64, FAKE, fd.FD_F32, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_lse_combine(FAKE, FAKE, 4, 0, 64, FAKE, fd.FD_F32, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_lse_combine(FAKE, FAKE, 4, 4, 513, FAKE, fd.FD_F32, None, None) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_lse_combine(None, FAKE, 4, 4, 64, FAKE, fd.FD_F32, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_lse_combine(FAKE, FAKE, 4, 4, 64, 0x10001, fd.FD_F32, None, None) == fd.FD_ERR_INVALID_ARG
+
+
+def test_workspace_size_is_pure_host_when_splits_forced(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.fd_decode_attn_workspace_size(2, 8, 2, 128, 4096, fd.FD_BF16, 1, ctypes.byref(n)) == fd.FD_OK
+    assert n.value == 0
+    assert lib.fd_decode_attn_workspace_size(2, 8, 2, 128, 4096, fd.FD_BF16, 16, ctypes.byref(n)) == fd.FD_OK
+    rows = 2 * 8
+    assert n.value >= rows * 16 * (128 + 1) * 4
+    assert lib.fd_decode_attn_workspace_size(2, 8, 2, 100, 4096, fd.FD_BF16, 16,
+                                             ctypes.byref(n)) == fd.FD_ERR_UNSUPPORTED
+
+
+def test_no_device_is_reported_not_fatal(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible")
+    n = ctypes.c_int32(0)
+    assert lib.fd_device_cu_count(ctypes.byref(n)) == fd.FD_ERR_HIP
+    assert lib.fd_last_error_message().decode()
+    # the planner path of the real call reports the same, without aborting
+    assert _decode(lib, n_splits=0) == fd.FD_ERR_HIP

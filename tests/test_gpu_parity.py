@@ -1,0 +1,155 @@
+"""HIP path against the fp64 oracle, through the C ABI (needs the GPU).
+
+Tolerances: max-abs 1e-5 for fp32 inputs and 1e-2 for bf16 inputs with fp32
+accumulation, on every output element (lse too, with the same bound).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_cases import max_abs, oracle_decode_rows, to_dev, to_host
+from workloads import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+def run_decode(fd, case, dtype, n_splits=0, out_dtype=None, scale=0.0):
+    q, k, v = (to_dev(case[x], dtype) for x in ("q", "k", "v"))
+    lens = torch.from_numpy(case["lens"]).to("cuda")
+    out, lse = fd.decode_attn(q, k, v, lens, n_splits=n_splits, out_dtype=out_dtype, scale=scale,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(lse)
+
+
+def check_decode(fd, case, dtype, n_splits=0, out_dtype=None, scale=None, tol=None):
+    out, lse = run_decode(fd, case, dtype, n_splits, out_dtype, scale or 0.0)
+    ref_out, ref_lse = oracle.attention(case["q"], case["k"], case["v"], case["lens"], scale)
+    tol = tol or TOL[dtype]
+    e_out, e_lse = max_abs(out, ref_out), max_abs(lse, ref_lse)
+    print(f"  n_splits={n_splits} max-abs out {e_out:.3e} lse {e_lse:.3e}", flush=True)
+    assert e_out <= tol, f"out error {e_out} > {tol}"
+    assert e_lse <= tol, f"lse error {e_lse} > {tol}"
+    return out
+
+
+# --------------------------------------------------------------------- tiny
+
+@pytest.mark.parametrize("n_splits", [4, 1, 2, 3, 7, 16, 32, 64, 0])
+def test_tiny_fp32_split_sweep(fd, n_splits):
+    w = configs.TINY
+    case = synth.decode_case(w.batch, w.q_heads, w.kv_heads, w.head_dim, w.max_len, w.dtype, w.seed)
+    check_decode(fd, case, "fp32", n_splits=n_splits, tol=w.tol)
+
+
+# ------------------------------------------------------ shapes and dtypes
+
+SHAPES = [
+    # B, Hq, Hkv, D, Lmax, dtype, lens
+    (3, 16, 2, 128, 3000, "bf16", [1, 1777, 3000]),
+    (4, 8, 8, 128, 2048, "bf16", (1024, 2048)),
+    (2, 8, 2, 64, 1500, "bf16", [1500, 333]),
+    (2, 4, 4, 128, 900, "fp32", [17, 900]),
+    (2, 8, 4, 64, 777, "fp32", [777, 400]),
+    (2, 32, 2, 128, 1200, "bf16", [1200, 650]),      # G = 16: two row blocks per KV head
+    (1, 32, 1, 128, 2100, "bf16", [2100]),           # MQA, G = 32
+    (2, 12, 4, 128, 640, "bf16", [640, 129]),        # G = 3
+    (5, 6, 6, 64, 300, "fp32", [1, 15, 16, 17, 300]),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_hq{s[1]}_hkv{s[2]}_d{s[3]}_l{s[4]}_{s[5]}")
+@pytest.mark.parametrize("n_splits", [0, 1, 5, 33])
+def test_decode_shapes(fd, shape, n_splits):
+    B, Hq, Hkv, D, L, dt, lens = shape
+    case = synth.decode_case(B, Hq, Hkv, D, L, dt, seed=1000 + B * 7 + Hq, lens=lens)
+    check_decode(fd, case, dt, n_splits=n_splits)
+
+
+@pytest.mark.parametrize("lens_one", [1, 15, 16, 17, 255, 256, 257, 1023, 1024])
+def test_boundary_lengths(fd, lens_one):
+    case = synth.decode_case(2, 16, 2, 128, 1024, "bf16", seed=77, lens=[lens_one, 1024])
+    for ns in (0, 4):
+        check_decode(fd, case, "bf16", n_splits=ns)
+
+
+def test_bf16_output_and_explicit_scale(fd):
+    case = synth.decode_case(2, 8, 2, 128, 1000, "bf16", seed=91, lens=[1000, 501])
+    check_decode(fd, case, "bf16", n_splits=3, out_dtype=torch.float32, scale=0.05)
+    check_decode(fd, case, "bf16", n_splits=3, out_dtype=torch.bfloat16)
+
+
+def test_padding_rows_are_never_read(fd):
+    # NaN in every row at or beyond lens must leave the output finite and equal
+    case = synth.decode_case(2, 16, 2, 128, 2048, "bf16", seed=5, lens=[700, 1301], pad_nan=True)
+    clean = dict(case)
+    for key in ("k", "v"):
+        clean[key] = np.where(np.isnan(case[key]), 0.0, case[key]).astype(np.float32)
+    a, _ = run_decode(fd, case, "bf16", n_splits=7)
+    b, _ = run_decode(fd, clean, "bf16", n_splits=7)
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b)
+
+
+def test_bitwise_repeatable(fd):
+    case = synth.decode_case(2, 16, 2, 128, 4096, "bf16", seed=6, lens=[4096, 3000])
+    outs = [run_decode(fd, case, "bf16", n_splits=9)[0] for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+# ------------------------------------------------------------ combine op
+
+def test_lse_combine_matches_oracle(fd):
+    rng = np.random.Generator(np.random.PCG64(12))
+    rows, P, D = 37, 19, 128
+    o = rng.standard_normal((rows, P, D)).astype(np.float32)
+    lse = (rng.standard_normal((rows, P)) * 5).astype(np.float32)
+    empty = rng.random((rows, P)) < 0.3
+    empty[:, 3] = False                    # every row keeps one finite piece
+    lse[empty] = -np.inf
+    o[np.isneginf(lse)] = 0.0
+    out, l = fd.lse_combine(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(), return_lse=True)
+    ref_o, ref_l = oracle.lse_combine(np.moveaxis(o, 1, 0), lse.T)
+    assert max_abs(to_host(out), ref_o) <= 1e-5
+    assert max_abs(to_host(l), ref_l) <= 1e-5
+
+
+# ------------------------------------------------------------ bifurcated
+
+@pytest.mark.parametrize("shape", [
+    # S, Hq, Hkv, D, Lc, Ldmax, dec_lens
+    (5, 8, 2, 128, 700, 64, [64, 0, 1, 33, 17]),
+    (8, 32, 1, 128, 1024, 40, (1, 40)),
+    (6, 32, 8, 128, 2000, 100, (1, 100)),
+    (3, 4, 4, 64, 300, 16, [16, 0, 5]),
+], ids=lambda s: f"S{s[0]}_hq{s[1]}_hkv{s[2]}_lc{s[4]}_ld{s[5]}")
+def test_bifurcated_small(fd, shape):
+    S, Hq, Hkv, D, Lc, Ld, dl = shape
+    case = synth.bifurcated_case(S, Hq, Hkv, D, Lc, Ld, "bf16", seed=2000 + S, dec_lens=dl)
+    t = {k: to_dev(case[k], "bf16") for k in ("q", "k_ctx", "v_ctx", "k_dec", "v_dec")}
+    dlen = torch.from_numpy(case["dec_lens"]).cuda()
+    out, lse = fd.bifurcated_attn(t["q"], t["k_ctx"], t["v_ctx"], t["k_dec"], t["v_dec"], dlen,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.bifurcated_attention(case["q"], case["k_ctx"], case["v_ctx"], case["k_dec"],
+                                               case["v_dec"], case["dec_lens"])
+    e_o, e_l = max_abs(to_host(out), ref_o), max_abs(to_host(lse), ref_l)
+    print(f"  bifurcated max-abs out {e_o:.3e} lse {e_l:.3e}", flush=True)
+    assert e_o <= 1e-2 and e_l <= 1e-2
+
+
+def test_bifurcated_equals_decode_on_concatenated_cache(fd):
+    S, Hq, Hkv, D, Lc, Ld = 4, 16, 2, 128, 1500, 80
+    case = synth.bifurcated_case(S, Hq, Hkv, D, Lc, Ld, "bf16", seed=31, dec_lens=[80, 3, 0, 41])
+    t = {k: to_dev(case[k], "bf16") for k in ("q", "k_ctx", "v_ctx", "k_dec", "v_dec")}
+    dlen = torch.from_numpy(case["dec_lens"]).cuda()
+    bif = fd.bifurcated_attn(t["q"], t["k_ctx"], t["v_ctx"], t["k_dec"], t["v_dec"], dlen)
+    kc = torch.cat([t["k_ctx"].unsqueeze(0).expand(S, -1, -1, -1), t["k_dec"]], dim=2).contiguous()
+    vc = torch.cat([t["v_ctx"].unsqueeze(0).expand(S, -1, -1, -1), t["v_dec"]], dim=2).contiguous()
+    cat = fd.decode_attn(t["q"], kc, vc, (dlen + Lc).to(torch.int32))
+    torch.cuda.synchronize()
+    assert max_abs(to_host(bif), to_host(cat)) <= 2e-3

@@ -1,0 +1,105 @@
+"""The five named workloads at full size, in the launch configuration the
+bench times (planner-chosen split counts), against the fp64 oracle.
+
+Inputs are drawn on the device (torch's seeded generator); the exact bits
+of the sampled (sequence, KV head) units are copied back for the oracle,
+which computes those units one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_cases import max_abs, oracle_decode_rows, to_host
+from workloads import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def make_decode(w, pad_nan=True):
+    dev = "cuda"
+    q = synth.device_normal((w.batch, w.q_heads, w.head_dim), w.seed, w.dtype, dev)
+    k = synth.device_normal((w.batch, w.kv_heads, w.max_len, w.head_dim), w.seed + 1, w.dtype, dev)
+    v = synth.device_normal((w.batch, w.kv_heads, w.max_len, w.head_dim), w.seed + 2, w.dtype, dev)
+    if w.ragged:
+        lens = synth.device_lengths(w.batch, w.max_len // 2, w.max_len, w.seed + 7, dev)
+    else:
+        lens = torch.full((w.batch,), w.max_len, dtype=torch.int32, device=dev)
+    if pad_nan:
+        for b, n in enumerate(lens.tolist()):
+            k[b, :, n:] = float("nan")
+            v[b, :, n:] = float("nan")
+    return q, k, v, lens
+
+
+def sampled_units(w, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    units = {(0, 0), (w.batch - 1, w.kv_heads - 1)}
+    while len(units) < min(count, w.batch * w.kv_heads):
+        units.add((int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))))
+    return sorted(units)
+
+
+@pytest.mark.parametrize("w", [configs.TINY, configs.CODELLAMA34B_SHARE] + list(configs.MHA_SWEEP),
+                         ids=lambda w: w.name)
+def test_decode_workload_full_size(fd, w):
+    print(f"  workload {w.name}", flush=True)
+    q, k, v, lens = make_decode(w)
+    out, lse = fd.decode_attn(q, k, v, lens, n_splits=w.n_splits, return_lse=True)
+    torch.cuda.synchronize()
+    out_h, lse_h = to_host(out), to_host(lse)
+    assert np.all(np.isfinite(out_h))
+    G = w.q_heads // w.kv_heads
+    units = sampled_units(w, 6, w.seed)
+    ref = oracle_decode_rows(q, k, v, lens, units)
+    worst = 0.0
+    for (b, g), (ro, rl) in ref.items():
+        rows = slice(g * G, (g + 1) * G)
+        worst = max(worst, max_abs(out_h[b, rows], ro), max_abs(lse_h[b, rows], rl))
+    print(f"  {len(units)} units, max-abs {worst:.3e} (tol {w.tol})", flush=True)
+    assert worst <= w.tol
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
+def make_bifurcated(w):
+    dev = "cuda"
+    S, Hq, Hkv, D = w.samples, w.q_heads, w.kv_heads, w.head_dim
+    t = {
+        "q": synth.device_normal((S, Hq, D), w.seed, w.dtype, dev),
+        "k_ctx": synth.device_normal((Hkv, w.ctx_len, D), w.seed + 1, w.dtype, dev),
+        "v_ctx": synth.device_normal((Hkv, w.ctx_len, D), w.seed + 2, w.dtype, dev),
+        "k_dec": synth.device_normal((S, Hkv, w.dec_max, D), w.seed + 3, w.dtype, dev),
+        "v_dec": synth.device_normal((S, Hkv, w.dec_max, D), w.seed + 4, w.dtype, dev),
+    }
+    dl = synth.device_lengths(S, w.dec_lo, w.dec_max, w.seed + 7, dev)
+    for s, n in enumerate(dl.tolist()):
+        t["k_dec"][s, :, n:] = float("nan")
+        t["v_dec"][s, :, n:] = float("nan")
+    return t, dl
+
+
+@pytest.mark.parametrize("w", configs.ALL_BIFURCATED, ids=lambda w: w.name)
+def test_bifurcated_workload_full_size(fd, w):
+    print(f"  workload {w.name}", flush=True)
+    t, dl = make_bifurcated(w)
+    out, lse = fd.bifurcated_attn(t["q"], t["k_ctx"], t["v_ctx"], t["k_dec"], t["v_dec"], dl,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    out_h, lse_h = to_host(out), to_host(lse)
+    assert np.all(np.isfinite(out_h))
+    kc, vc = to_host(t["k_ctx"]), to_host(t["v_ctx"])
+    dl_h = dl.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    samples = sorted({0, w.samples - 1, int(np.argmin(dl_h)), *rng.integers(w.samples, size=3).tolist()})
+    worst = 0.0
+    for s in samples:
+        n = int(dl_h[s])
+        ro, rl = oracle.bifurcated_attention(to_host(t["q"][s:s + 1]), kc, vc,
+                                             to_host(t["k_dec"][s:s + 1, :, :max(n, 1)]),
+                                             to_host(t["v_dec"][s:s + 1, :, :max(n, 1)]),
+                                             np.array([n]))
+        worst = max(worst, max_abs(out_h[s:s + 1], ro), max_abs(lse_h[s:s + 1], rl))
+    print(f"  samples {samples}, max-abs {worst:.3e} (tol {w.tol})", flush=True)
+    assert worst <= w.tol
