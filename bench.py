@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one full decode-attention call: the split-KV partial kernel plus
+the LSE combine (or the single direct kernel when one piece suffices), over
+one set of synthetic inputs already resident in HBM.  Inputs rotate over
+enough distinct copies (>= 1 GiB in total) that no step can be served from
+the 256 MB Infinity Cache.
+
+Steps are captured in a HIP graph and timed with HIP events around its
+replay (host launch cost stays outside, as in a graph-captured decode loop).
+Prints ONE JSON line: value = achieved KV-read rate of the whole step
+(algorithmic KV bytes / step time, TB/s), ms_per_step, the roofline of the
+dominant kernel (its average duration from a graph of K launches of that
+kernel alone, timed the same way on the stream it runs on), and the fp64 CPU
+oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import configs, synth  # noqa: E402
+
+METRIC = "decode-attn µs/step + achieved KV-read HBM TB/s (fraction of MI355X peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+ROTATION_BYTES = 1 << 30
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_06_amd", "csrc", f)
+                  for f in ("fd_kernels.hip", "fd_mfma.hip", "fd_bifurcated.hip", "fd_device.h",
+                            "fd_internal.h", "fd_api.cpp")]
+
+WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_BIFURCATED)}
+DEFAULT_WORKLOAD = configs.CODELLAMA34B_SHARE.name
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        if os.path.exists(path):
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- inputs
+
+def decode_inputs(w, copies, dev):
+    import torch
+
+    sets = []
+    if w.ragged:
+        lens = synth.device_lengths(w.batch, w.max_len // 2, w.max_len, w.seed + 7, dev)
+    else:
+        lens = torch.full((w.batch,), w.max_len, dtype=torch.int32, device=dev)
+    for c in range(copies):
+        s = w.seed + 1000 * c
+        q = synth.device_normal((w.batch, w.q_heads, w.head_dim), s, w.dtype, dev)
+        k = synth.device_normal((w.batch, w.kv_heads, w.max_len, w.head_dim), s + 1, w.dtype, dev)
+        v = synth.device_normal((w.batch, w.kv_heads, w.max_len, w.head_dim), s + 2, w.dtype, dev)
+        sets.append((q, k, v))
+    return sets, lens
+
+
+def bifurcated_inputs(w, copies, dev):
+    sets = []
+    dl = synth.device_lengths(w.samples, w.dec_lo, w.dec_max, w.seed + 7, dev)
+    for c in range(copies):
+        s = w.seed + 1000 * c
+        sets.append({
+            "q": synth.device_normal((w.samples, w.q_heads, w.head_dim), s, w.dtype, dev),
+            "k_ctx": synth.device_normal((w.kv_heads, w.ctx_len, w.head_dim), s + 1, w.dtype, dev),
+            "v_ctx": synth.device_normal((w.kv_heads, w.ctx_len, w.head_dim), s + 2, w.dtype, dev),
+            "k_dec": synth.device_normal((w.samples, w.kv_heads, w.dec_max, w.head_dim), s + 3, w.dtype, dev),
+            "v_dec": synth.device_normal((w.samples, w.kv_heads, w.dec_max, w.head_dim), s + 4, w.dtype, dev),
+        })
+    return sets, dl
+
+
+# ------------------------------------------------------------- GPU timing
+
+def timed_graph(fn, steps):
+    """Capture fn(0..steps-1) into one HIP graph and time a replay with HIP
+    events on the stream it runs on; returns ms per step.  Host launch cost
+    is outside the timed region, as in a graph-captured decode loop."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(min(steps, 3)):
+            fn(j)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(steps):
+            fn(j)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    return ms
+
+
+def timed_eager(fn, steps):
+    """The same steps launched one by one from Python (includes host cost)."""
+    import torch
+
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for j in range(steps):
+        fn(j)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def time_decode(w, steps, warmup):
+    import torch
+
+    import decode_attention_06_amd as fd
+
+    dev = torch.device("cuda:0")
+    sz = 2 if w.dtype == "bf16" else 4
+    alloc_bytes = 2 * w.batch * w.kv_heads * w.max_len * w.head_dim * sz
+    copies = max(2, math.ceil(ROTATION_BYTES / alloc_bytes))
+    sets, lens = decode_inputs(w, copies, dev)
+    kv_bytes = 2 * int(lens.sum().item()) * w.kv_heads * w.head_dim * sz   # algorithmic, per step
+    dt = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
+    ns = w.n_splits if w.n_splits > 0 else fd.plan_splits(w.batch, w.q_heads, w.kv_heads, w.head_dim,
+                                                          w.max_len, dt, fd.device_cu_count())
+    rows = w.batch * w.q_heads
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
+    o_part = torch.empty((rows, ns, w.head_dim), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((rows, ns), dtype=torch.float32, device=dev)
+
+    def step(j):
+        q, k, v = sets[j % copies]
+        if ns == 1:
+            fd.decode_attn(q, k, v, lens, n_splits=1, out=out, workspace=o_part)
+        else:
+            fd.decode_attn_partials(q, k, v, ns, lens=lens, o_part=o_part, lse_part=lse_part)
+            fd.lse_combine(o_part.view(rows, ns, w.head_dim), lse_part, out=out.view(rows, w.head_dim))
+
+    def partial_only(j):
+        q, k, v = sets[j % copies]
+        if ns == 1:
+            fd.decode_attn(q, k, v, lens, n_splits=1, out=out, workspace=o_part)
+        else:
+            fd.decode_attn_partials(q, k, v, ns, lens=lens, o_part=o_part, lse_part=lse_part)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    eager_ms = timed_eager(step, steps)
+    step_ms = timed_graph(step, steps)
+    kern_ms = timed_graph(partial_only, steps)
+
+    # Plain read of the same number of bytes, rotated the same way.
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def probe(j):
+        q, k, v = sets[j % copies]
+        fd.read_probe(k, sink)
+        fd.read_probe(v, sink)
+
+    probe_ms = timed_graph(probe, steps)
+    probe_bytes = 2 * sets[0][1].numel() * sets[0][1].element_size()
+
+    info = {
+        "n_splits": ns, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": kern_ms,
+        "eager_step_ms": eager_ms, "probe_gbs": probe_bytes / (probe_ms * 1e-3) / 1e9,
+        "kernel": "partial_mfma_kernel" if (w.dtype == "bf16" and w.head_dim == 128 and
+                                             w.q_heads // w.kv_heads >= 4) else "partial_valu_kernel",
+        "flops": 4 * int(lens.sum().item()) * w.q_heads * w.head_dim,
+    }
+    host = [t.detach().float().cpu().numpy() for t in sets[0]]
+    return info, (host, lens.cpu().numpy())
+
+
+def time_bifurcated(w, steps, warmup):
+    import torch
+
+    import decode_attention_06_amd as fd
+
+    dev = torch.device("cuda:0")
+    sz = 2
+    alloc = (2 * w.kv_heads * w.ctx_len + 2 * w.samples * w.kv_heads * w.dec_max) * w.head_dim * sz
+    copies = max(2, math.ceil(ROTATION_BYTES / alloc))
+    sets, dl = bifurcated_inputs(w, copies, dev)
+    n_dec = int(dl.sum().item())
+    kv_bytes = (2 * w.kv_heads * w.ctx_len + 2 * n_dec * w.kv_heads) * w.head_dim * sz
+    flops = 4 * w.q_heads * w.head_dim * (w.samples * w.ctx_len + n_dec)
+    out = torch.empty((w.samples, w.q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    wsb = fd.bifurcated_workspace_size(w.samples, w.q_heads, w.kv_heads, w.head_dim, w.ctx_len, w.dec_max,
+                                       fd.FD_BF16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def step(j):
+        t = sets[j % copies]
+        fd.bifurcated_attn(t["q"], t["k_ctx"], t["v_ctx"], t["k_dec"], t["v_dec"], dl, out=out, workspace=ws)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    eager_ms = timed_eager(step, steps)
+    step_ms = timed_graph(step, steps)
+    info = {"n_splits": None, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": step_ms,
+            "eager_step_ms": eager_ms, "probe_gbs": None, "kernel": "bifurcated (whole call)", "flops": flops}
+    return info, None
+
+
+# --------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, host_inputs, kv_bytes, budget_s):
+    """Time the fp64 oracle on the host cores for one full step of w."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    (q, k, v), lens = host_inputs
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    runs, total = 0, 0.0
+    while runs < 1 or (total < budget_s and runs < 50):
+        t = time.perf_counter()
+        oracle.attention(q, k, v, lens)
+        total += time.perf_counter() - t
+        runs += 1
+    per_step = total / runs
+    return {
+        "value": kv_bytes / per_step / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{runs} full step(s) of {w.name} (inputs already in host memory as float64), "
+                  f"{per_step * 1e3:.1f} ms per step",
+    }
+
+
+def counters_for(kernel, workload):
+    """HBM traffic per launch from committed rocprofv3 counter runs, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("entries", {}).get(f"{kernel}|{workload}")
+    if not entry or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("traffic_bytes")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return 0
+    if args.calibrate_copy:
+        import torch
+
+        src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.calibrate_copy << 20, "copies": 5}))
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible GPU", file=sys.stderr)
+        return 1
+    import decode_attention_06_amd as fd
+
+    fd.load()
+    w = WORKLOADS[args.workload]
+    bif = w.name in {b.name for b in configs.ALL_BIFURCATED}
+    if bif:
+        info, host = time_bifurcated(w, args.steps, args.warmup)
+        dtype = w.dtype
+    else:
+        info, host = time_decode(w, args.steps, args.warmup)
+        dtype = w.dtype
+    step_s = info["step_ms"] * 1e-3
+    kern_s = info["kernel_ms"] * 1e-3
+    achieved_gbs = info["kv_bytes"] / kern_s / 1e9
+    value_tbs = info["kv_bytes"] / step_s / 1e12
+    log(f"[bench] {w.name}: step {info['step_ms'] * 1e3:.2f} us in a graph (launched eagerly from Python: "
+        f"{info['eager_step_ms'] * 1e3:.2f} us), dominant kernel {info['kernel_ms'] * 1e3:.2f} us, "
+        f"n_splits={info['n_splits']}, plain read of the same bytes: {info['probe_gbs']} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline and host is not None and int(os.environ.get("RANK", "0")) == 0:
+        cpu = cpu_baseline(w, host, info["kv_bytes"], args.cpu_seconds)
+
+    config = {"workload": w.name, "kv_bytes_per_step": info["kv_bytes"], "n_splits": info["n_splits"],
+              "input_copies": info["copies"], "timing": "HIP events around a graph replay of the K steps; inputs rotated over >= 1 GiB",
+              "eager_us_per_step": round(info["eager_step_ms"] * 1e3, 3)}
+    if bif:
+        config.update(samples=w.samples, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                      ctx_len=w.ctx_len, dec_len=f"{w.dec_lo}..{w.dec_max}")
+    else:
+        config.update(batch=w.batch, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                      kv_len=w.max_len, lens="uniform [L/2, L]" if w.ragged else "all L")
+    line = {
+        "metric": METRIC,
+        "value": round(value_tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(info["step_ms"], 6),
+        "us_per_step": round(info["step_ms"] * 1e3, 3),
+        "frac_of_hbm_peak": round(value_tbs * 1000 / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic N(0,1) inputs, seeded",
+        "config": config,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": info["kernel"],
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": counters_for(info["kernel"], w.name),
+            "kernel_us": round(info["kernel_ms"] * 1e3, 3),
+            "read_probe_gbs": None if info["probe_gbs"] is None else round(info["probe_gbs"], 1),
+        },
+        "cpu_baseline": cpu,
+    }
+    if bif:
+        line["roofline"]["mfma_tflops"] = round(info["flops"] / step_s / 1e12, 2)
+        line["roofline"]["mfma_frac"] = round(info["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

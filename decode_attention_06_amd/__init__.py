@@ -33,6 +33,9 @@ SIGNATURES = {
     "fd_bifurcated_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i64, _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
     "fd_lse_combine": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "fd_decode_attn_partials": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                         _c_i32, _c_i32, _c_vp, _c_vp, _c_f32, _c_vp]),
+    "fd_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_vp]),
 }
 
 _lib = None
@@ -218,3 +221,28 @@ def lse_combine(o_part, lse_part, out=None, out_dtype=None, return_lse=False, st
     _check(lib.fd_lse_combine(_dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"), rows, P, D,
                               _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def decode_attn_partials(q, k, v, n_splits, lens=None, o_part=None, lse_part=None, scale=0.0, stream=None):
+    """fd_decode_attn_partials: per-piece outputs [B*Hq, n_splits, D] and lse [B*Hq, n_splits]."""
+    torch = _torch()
+    lib = load()
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k.shape
+    dt = _dtype_code(q)
+    rows = B * Hq
+    if o_part is None:
+        o_part = torch.empty((rows, n_splits, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((rows, n_splits), dtype=torch.float32, device=q.device)
+    _check(lib.fd_decode_attn_partials(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                       _opt_ptr(lens, "lens"), B, Hq, Hkv, D, Lmax, dt, int(n_splits),
+                                       _dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"),
+                                       float(scale), _stream(stream)))
+    return o_part, lse_part
+
+
+def read_probe(buf, sink, stream=None):
+    """fd_read_probe: stream a device buffer once (HBM read-rate measurement)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().fd_read_probe(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink"), _stream(stream)))

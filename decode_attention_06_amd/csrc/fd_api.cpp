@@ -9,6 +9,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -88,6 +90,39 @@ float resolve_scale(float scale, int32_t D) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Smallest GQA group that goes to the matrix-core kernel (bf16, D = 128).
+constexpr int kMfmaMinGroup = 4;
+
+// Which partial kernel serves a (dtype, D, G) call, and how many query-row
+// blocks each KV head is cut into.  FD_PARTIAL_KERNEL=valu|mfma overrides
+// the choice where both kernels support the shape (used to compare them).
+struct Path {
+    bool mfma;
+    int rows_per_block;
+    int row_blocks;
+};
+
+Path choose_path(int32_t dtype, int32_t D, int G) {
+    const bool mfma_ok = dtype == FD_BF16 && D == 128;
+    bool mfma = mfma_ok && G >= kMfmaMinGroup;
+    if (mfma_ok) {
+        if (const char* env = std::getenv("FD_PARTIAL_KERNEL")) {
+            if (!std::strcmp(env, "valu")) mfma = false;
+            if (!std::strcmp(env, "mfma")) mfma = true;
+        }
+    }
+    Path path;
+    path.mfma = mfma;
+    path.rows_per_block = mfma ? fd::mfma_rows_per_block(G) : fd::valu_rows_per_block(G);
+    path.row_blocks = (G + path.rows_per_block - 1) / path.rows_per_block;
+    return path;
+}
+
+hipError_t launch_partial(const fd::PartialParams& p, const Path& path, int32_t dtype, int32_t D,
+                          hipStream_t s) {
+    return path.mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, dtype, D, path.rows_per_block, s);
+}
+
 // Pieces for the context and for the decode part of a bifurcated call.
 void plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld,
                      int32_t dtype, int32_t n_cu, int32_t* pc, int32_t* pd) {
@@ -120,7 +155,7 @@ int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
         n_cu <= 0 || num_q_heads % num_kv_heads != 0 || (dtype != FD_F32 && dtype != FD_BF16))
         return -1;
     const int G = num_q_heads / num_kv_heads;
-    const int64_t units = int64_t(batch) * num_kv_heads * (G / fd::valu_rows_per_block(G));
+    const int64_t units = int64_t(batch) * num_kv_heads * choose_path(dtype, head_dim, G).row_blocks;
     const int64_t target = int64_t(n_cu) * kWgPerCu;
     if (units >= target) return 1;
     int64_t s = (target + units - 1) / units;
@@ -205,8 +240,7 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
             return fail(FD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total());
     }
 
-    const int G = Hq / Hkv;
-    const int GB = fd::valu_rows_per_block(G);
+    const Path path = choose_path(dtype, D, Hq / Hkv);
     fd::PartialParams p{};
     p.q = q;
     p.k = k;
@@ -221,7 +255,7 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.n_splits = ns;
-    p.row_blocks = G / GB;
+    p.row_blocks = path.row_blocks;
     p.scale_log2 = resolve_scale(scale, D) * kLog2e;
     p.out_bf16 = out_dtype == FD_BF16;
     p.direct = ns == 1;
@@ -236,12 +270,60 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
         p.part_offset = 0;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    hipError_t e = launch_partial(p, path, dtype, D, s);
     if (e != hipSuccess) return hip_fail(e, "split-KV partial kernel launch");
     if (ns > 1) {
         e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), ns, D, out, p.out_bf16, lse_out, s);
         if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
     }
+    return FD_OK;
+}
+
+fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, const int32_t* lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
+                                  int32_t dtype, int32_t n_splits, float* o_part, float* lse_part,
+                                  float scale, void* stream) {
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    if (n_splits <= 0) return fail(FD_ERR_INVALID_ARG, "n_splits must be given (> 0) for the partial stage");
+    FD_TRY(check_ptr(q, 16, "q"));
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    FD_TRY(check_ptr(o_part, 16, "o_part"));
+    FD_TRY(check_ptr(lse_part, 4, "lse_part"));
+    if (lens && !aligned(lens, 4)) return fail(FD_ERR_INVALID_ARG, "lens is not 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
+
+    const Path path = choose_path(dtype, D, Hq / Hkv);
+    fd::PartialParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lens = lens;
+    p.Lmax = Lmax;
+    p.kv_stride_h = Lmax * D;
+    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.n_splits = n_splits;
+    p.row_blocks = path.row_blocks;
+    p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+    p.direct = 0;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.part_stride = n_splits;
+    p.part_offset = 0;
+    hipError_t e = launch_partial(p, path, dtype, D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "split-KV partial kernel launch");
+    return FD_OK;
+}
+
+fd_status fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    FD_TRY(check_ptr(buf, 16, "buf"));
+    FD_TRY(check_ptr(sink, 4, "sink"));
+    if (bytes == 0 || bytes % 16 != 0) return fail(FD_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    hipError_t e = fd::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "read probe kernel launch");
     return FD_OK;
 }
 
@@ -291,6 +373,7 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     int32_t pc = 0, pd = 0;
     plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus, &pc, &pd);
     const int32_t P = pc + pd;
+    if (P > FD_MAX_PARTS) return fail(FD_ERR_UNSUPPORTED, "%d pieces exceed the combine limit %d", P, FD_MAX_PARTS);
     const int64_t rows = int64_t(S) * Hq;
     const PartialLayout L = partial_layout(rows, P, D);
     if (workspace_bytes < L.total())
@@ -298,8 +381,7 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     float* lse_part = static_cast<float*>(workspace);
     float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_bytes);
 
-    const int G = Hq / Hkv;
-    const int GB = fd::valu_rows_per_block(G);
+    const Path path = choose_path(dtype, D, Hq / Hkv);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // Context part: every sample reads the same [Hkv, Lc, D] rows (batch
@@ -318,12 +400,12 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.n_splits = pc;
-    p.row_blocks = G / GB;
+    p.row_blocks = path.row_blocks;
     p.part_stride = P;
     p.part_offset = 0;
     p.scale_log2 = resolve_scale(scale, D) * kLog2e;
     p.direct = 0;
-    hipError_t e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    hipError_t e = launch_partial(p, path, dtype, D, s);
     if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
 
     // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
@@ -335,7 +417,7 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     p.kv_stride_b = int64_t(Hkv) * Ld * D;
     p.n_splits = pd;
     p.part_offset = pc;
-    e = fd::launch_partial_valu(p, dtype, D, GB, s);
+    e = launch_partial(p, path, dtype, D, s);
     if (e != hipSuccess) return hip_fail(e, "bifurcated decode kernel launch");
 
     e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), P, D, out, out_dtype == FD_BF16, lse_out, s);
@@ -347,6 +429,7 @@ fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t row
                          int32_t D, void* out, int32_t out_dtype, float* lse_out, void* stream) {
     if (rows <= 0 || n_parts <= 0) return fail(FD_ERR_INVALID_ARG, "rows and n_parts must be positive");
     if (D <= 0 || D > 512) return fail(FD_ERR_UNSUPPORTED, "head_dim %d outside [1, 512]", D);
+    if (n_parts > FD_MAX_PARTS) return fail(FD_ERR_UNSUPPORTED, "n_parts %d above %d", n_parts, FD_MAX_PARTS);
     FD_TRY(check_out_dtype(out_dtype));
     FD_TRY(check_ptr(o_part, 4, "o_part"));
     FD_TRY(check_ptr(lse_part, 4, "lse_part"));

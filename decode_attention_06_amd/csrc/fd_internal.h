@@ -7,6 +7,9 @@
 
 namespace fd {
 
+// Most pieces one combine can merge per output row (LDS holds their weights).
+#define FD_MAX_PARTS 4096
+
 // One launch of the split-KV partial kernel.  A work unit is
 // (sequence b, KV head, block of query rows, piece); every unit streams its
 // piece of the KV rows once and keeps a running max / running sum per query
@@ -39,8 +42,19 @@ inline int valu_rows_per_block(int G) {
     return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
+// Rows per work unit of the matrix-core kernel (16 or 32) for a group of G.
+int mfma_rows_per_block(int G);
+
+// Matrix-core partial kernel: bf16, head_dim 128, any G (row_blocks =
+// ceil(G / mfma_rows_per_block(G))).
+hipError_t launch_partial_mfma(const PartialParams& p, hipStream_t stream);
+
 hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, int rows_per_block,
                                hipStream_t stream);
+
+// Streams `bytes` (multiple of 16) with 16-byte loads and folds them into
+// one word written to sink[0] only if it equals a sentinel.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                               int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,

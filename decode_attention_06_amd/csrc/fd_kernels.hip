@@ -23,26 +23,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "fd_device.h"
 #include "fd_internal.h"
 
 namespace fd {
 namespace {
-
-constexpr float kLn2 = 0.693147180559945309417f;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Raw bf16 bits -> float (exact).
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
 // Unpack one 16-byte vector of storage type T into floats.
 template <typename T>
@@ -70,11 +55,6 @@ struct Vec16<uint16_t> {  // bf16 bits
     }
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
 // Sum over each aligned group of LPR lanes; every lane of the group ends
 // with the same bits (each step adds a pair in both orders, and float
 // addition commutes).  DPP: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -87,13 +67,6 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (LPR >= 16) x += dpp<0x140>(x);
     if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
     return x;
-}
-
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float v, int bf16) {
-    if (bf16)
-        static_cast<uint16_t*>(out)[idx] = to_bf16(v);
-    else
-        static_cast<float*>(out)[idx] = v;
 }
 
 // Merge running state (m2, l2) into (m, l); returns the weights applied to
@@ -121,7 +94,8 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     __shared__ float s_l[NW][GB];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
     const int r = lane / LPR, c = lane % LPR;
 
     int idx = blockIdx.x;
@@ -166,17 +140,14 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 
     for (int tb = t0 + wave * WAVE_TOK; tb < t1; tb += WG_TOK) {
         const bool full = tb + WAVE_TOK <= t1;
+        // Unconditional loads; rows at or beyond t1 clamp to t1 - 1 (a valid
+        // row whose score is masked below), so the loads issue back to back.
         uint4 kr[U], vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = tb + u * RPW + r;
-            if (full || t < t1) {
-                kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
-                vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
+            const int t = min(tb + u * RPW + r, t1 - 1);
+            kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
+            vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
         }
 
         // Scores (log2 domain).  All lanes take part in the DPP sums.
@@ -278,7 +249,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
             }
         }
         const float o = (L > 0.f) ? A / L : 0.f;
-        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
         const int64_t row = (int64_t)b * p.Hq + h0 + g;
         if (p.direct) {
             store_out(p.out, row * D + d, o, p.out_bf16);
@@ -291,62 +262,163 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     }
 }
 
-// LSE combine: one workgroup per (row, 32-wide slice of D).  Thread
-// (pg, dl) sums pieces pg, pg+8, ... for column slice*32 + dl; the eight
-// partial sums are then added in a fixed order.
-constexpr int CMB_SLICE = 32;
-constexpr int CMB_GROUPS = 8;
+// LSE combine ([FD] "Por qué la decodificación necesita otra
+// planificación": the reduction that renormalises the pieces).  One
+// workgroup per (row, slice of CMB_SLICE columns); thread (part group pg,
+// column vector dv) handles pieces pg, pg + GROUPS, ...  The first batch of
+// partial outputs is requested together with the row's lse values, so a row
+// with up to 8 * GROUPS pieces costs one memory round trip.  Piece weights are
+// exp(lse_i - max lse); sums run in a fixed order (bitwise repeatable).
+constexpr int CMB_THREADS = 256;
+constexpr int CMB_SLICE = 32;                   // columns per workgroup
+constexpr int CMB_BATCH = 8;                    // pieces in flight per thread
 
-__global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restrict__ o_part,
-                                                          const float* __restrict__ lse_part,
-                                                          int32_t n_parts, int32_t D, void* out,
-                                                          int32_t out_bf16, float* lse_out) {
-    __shared__ float s_red[256];
-    __shared__ float s_acc[CMB_GROUPS][CMB_SLICE];
-    __shared__ float s_w[CMB_GROUPS];
-    constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < CMB_THREADS / 64; ++k) r = fmaxf(r, red[k]);
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < CMB_THREADS / 64; ++k) r += red[k];
+    return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float* src, float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(src);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = src[e];
+    }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* __restrict__ o_part,
+                                                                  const float* __restrict__ lse_part,
+                                                                  int32_t n_parts, int32_t D, void* out,
+                                                                  int32_t out_bf16, float* lse_out) {
+    constexpr int DL = CMB_SLICE / VEC;         // threads across the slice
+    constexpr int GROUPS = CMB_THREADS / DL;    // part groups
+    __shared__ float s_red[CMB_THREADS / 64];
+    __shared__ float s_acc[GROUPS][CMB_SLICE];
 
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
-    const int slice = blockIdx.y;
     const float* lrow = lse_part + row * n_parts;
+    const int dv = tid % DL, pg = tid / DL;
+    const int d0 = blockIdx.y * CMB_SLICE + dv * VEC;
+    const bool col_ok = d0 < D;
+    const float* obase = o_part + row * (int64_t)n_parts * D + d0;
 
-    // Row maximum of the piece lse values.
-    float M = -INFINITY;
-    for (int i = tid; i < n_parts; i += 256) M = fmaxf(M, lrow[i]);
-    s_red[tid] = M;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) s_red[tid] = fmaxf(s_red[tid], s_red[tid + s]);
-        __syncthreads();
-    }
-    M = s_red[0];
-
-    const int dl = tid % CMB_SLICE, pg = tid / CMB_SLICE;
-    const int d = slice * CMB_SLICE + dl;
-    float A = 0.f, W = 0.f;
-    if (M != -INFINITY) {
-        for (int i = pg; i < n_parts; i += CMB_GROUPS) {
-            const float li = lrow[i];
-            const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2e);
-            W += w;
-            if (d < D) A = fmaf(w, o_part[(row * n_parts + i) * D + d], A);
-        }
-    }
-    s_acc[pg][dl] = A;
-    if (dl == 0) s_w[pg] = W;
-    __syncthreads();
-    if (pg == 0 && d < D) {
-        float a = 0.f, z = 0.f;
+    // Batch 0: partial outputs and their lse, requested together.
+    float ov[CMB_BATCH][VEC], lv[CMB_BATCH];
 #pragma unroll
-        for (int g = 0; g < CMB_GROUPS; ++g) {
-            a += s_acc[g][dl];
-            z += s_w[g];
-        }
-        const float o = (z > 0.f) ? a / z : 0.f;
-        store_out(out, row * D + d, o, out_bf16);
-        if (d == 0 && lse_out) lse_out[row] = (z > 0.f) ? M + logf(z) : -INFINITY;
+    for (int u = 0; u < CMB_BATCH; ++u) {
+        const int i = pg + u * GROUPS;
+        lv[u] = (i < n_parts) ? lrow[i] : -INFINITY;
+        if (i < n_parts && col_ok)
+            load_vec<VEC>(obase + (int64_t)i * D, ov[u]);
+        else
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ov[u][e] = 0.f;
     }
+    // Row maximum and weight sum over all pieces.
+    float M = -INFINITY;
+    for (int i = tid; i < n_parts; i += CMB_THREADS) M = fmaxf(M, lrow[i]);
+    M = block_max(M, s_red);
+    float z = 0.f;
+    if (M != -INFINITY)
+        for (int i = tid; i < n_parts; i += CMB_THREADS) {
+            const float li = lrow[i];
+            z += (li == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2ef);
+        }
+    const float Z = block_sum(z, s_red);
+
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < CMB_BATCH; ++u) {
+            const float w = (lv[u] == -INFINITY) ? 0.f : fast_exp2((lv[u] - M) * kLog2ef);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+        }
+        for (int base = CMB_BATCH * GROUPS; base < n_parts; base += CMB_BATCH * GROUPS) {
+#pragma unroll
+            for (int u = 0; u < CMB_BATCH; ++u) {
+                const int i = base + pg + u * GROUPS;
+                lv[u] = (i < n_parts) ? lrow[i] : -INFINITY;
+                if (i < n_parts && col_ok)
+                    load_vec<VEC>(obase + (int64_t)i * D, ov[u]);
+                else
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) ov[u][e] = 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < CMB_BATCH; ++u) {
+                const float w = (lv[u] == -INFINITY) ? 0.f : fast_exp2((lv[u] - M) * kLog2ef);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s_acc[pg][dv * VEC + e] = acc[e];
+    __syncthreads();
+    if (tid < CMB_SLICE) {
+        const int d = blockIdx.y * CMB_SLICE + tid;
+        if (d < D) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < GROUPS; ++k) a += s_acc[k][tid];
+            store_out(out, row * D + d, (Z > 0.f) ? a / Z : 0.f, out_bf16);
+            if (d == 0 && lse_out) lse_out[row] = (Z > 0.f) ? M + logf(Z) : -INFINITY;
+        }
+    }
+}
+
+// HBM read ceiling: each workgroup streams one contiguous chunk of the
+// buffer with 16-byte loads, eight in flight per thread, and folds the data
+// into a word so the loads cannot be dropped.
+constexpr int PROBE_UNROLL = 8;
+constexpr size_t PROBE_CHUNK = 16384;          // bytes per workgroup
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ buf, size_t n16,
+                                                         uint32_t* sink) {
+    const size_t per_wg = PROBE_CHUNK / 16;
+    const size_t base = (size_t)blockIdx.x * per_wg;
+    const size_t end = min(base + per_wg, n16);
+    uint32_t acc = 0;
+    for (size_t i = base + threadIdx.x; i < end; i += 256 * PROBE_UNROLL) {
+        uint4 v[PROBE_UNROLL];
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u) {
+            const size_t j = min(i + (size_t)u * 256, end - 1);
+            v[u] = buf[j];
+        }
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
 template <typename T, int D>
@@ -377,12 +449,25 @@ hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, 
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    const size_t wgs = (bytes + PROBE_CHUNK - 1) / PROBE_CHUNK;
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       static_cast<const uint4*>(buf), n16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                               int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
                               float* lse_out, hipStream_t stream) {
     const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
-    hipLaunchKernelGGL(lse_combine_kernel, grid, dim3(256), 0, stream, o_part, lse_part, n_parts,
-                       head_dim, out, out_bf16, lse_out);
+    const bool vec4 = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(o_part) % 16 == 0);
+    if (vec4)
+        hipLaunchKernelGGL(lse_combine_kernel<4>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
+                           n_parts, head_dim, out, out_bf16, lse_out);
+    else
+        hipLaunchKernelGGL(lse_combine_kernel<1>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
+                           n_parts, head_dim, out, out_bf16, lse_out);
     return hipGetLastError();
 }
 

@@ -148,6 +148,27 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fd_decode_attn_partials - the partial stage of fd_decode_attn on its own
+ * ([FD] "Por qué la decodificación necesita otra planificación": every piece
+ * yields a partial output and its log-sum-exp).  Together with
+ * fd_lse_combine(o_part, lse_part, B*Hq, n_splits, D, ...) it computes
+ * exactly what fd_decode_attn computes; callers that split one sequence's
+ * history across several devices combine the pieces of all of them.
+ *
+ *   q, k, v, lens, shapes, dtype, scale: as in fd_decode_attn
+ *   n_splits  pieces per sequence, > 0 (no planner here)
+ *   o_part    device fp32 [B*Hq, n_splits, D], 16-byte aligned; piece i of
+ *             row (b, h) covers cache rows [i*c, min((i+1)*c, lens[b])) with
+ *             c = ceil(lens[b] / n_splits) rounded up to a multiple of 16
+ *   lse_part  device fp32 [B*Hq, n_splits]; -inf (with o_part = 0) marks an
+ *             empty piece
+ */
+fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, const int32_t* lens,
+                                  int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t max_len, int32_t dtype, int32_t n_splits,
+                                  float* o_part, float* lse_part, float scale, void* stream);
+
+/*
  * fd_bifurcated_attn_workspace_size - bytes of workspace fd_bifurcated_attn
  * needs: partials of every context piece and every decode piece,
  * [S, Hq, P, D] fp32 plus [S, Hq, P] fp32.
@@ -194,6 +215,16 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
 fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                          int32_t n_parts, int32_t head_dim, void* out, int32_t out_dtype,
                          float* lse_out, void* stream);
+
+/*
+ * fd_read_probe - measurement aid, not part of the attention path: streams
+ * `bytes` (a positive multiple of 16, buf 16-byte aligned) once with the
+ * 16-byte coalesced loads the partial kernels use and folds them into one
+ * word (sink, 4 bytes of device memory, is written only in a
+ * data-dependent corner case).  Timing it gives the HBM read rate this
+ * device actually sustains, the ceiling for the KV stream.
+ */
+fd_status fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,9 @@ SHAPES = [
     (2, 32, 2, 128, 1200, "bf16", [1200, 650]),      # G = 16: two row blocks per KV head
     (1, 32, 1, 128, 2100, "bf16", [2100]),           # MQA, G = 32
     (2, 12, 4, 128, 640, "bf16", [640, 129]),        # G = 3
+    (1, 24, 1, 128, 700, "bf16", [700]),             # G = 24: one 32-row matrix-core block
+    (2, 48, 1, 128, 500, "bf16", [500, 77]),         # G = 48: two 32-row blocks
+    (3, 64, 8, 128, 1100, "bf16", [1100, 64, 513]),  # G = 8
     (5, 6, 6, 64, 300, "fp32", [1, 15, 16, 17, 300]),
 ]
 
@@ -74,6 +77,17 @@ def test_decode_shapes(fd, shape, n_splits):
 def test_boundary_lengths(fd, lens_one):
     case = synth.decode_case(2, 16, 2, 128, 1024, "bf16", seed=77, lens=[lens_one, 1024])
     for ns in (0, 4):
+        check_decode(fd, case, "bf16", n_splits=ns)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16, 32])
+def test_both_partial_kernels(fd, monkeypatch, kernel, G):
+    # FD_PARTIAL_KERNEL forces one of the two partial kernels (bf16, D 128)
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", kernel)
+    Hkv = 2
+    case = synth.decode_case(2, G * Hkv, Hkv, 128, 1300, "bf16", seed=300 + G, lens=[1300, 555])
+    for ns in (1, 6):
         check_decode(fd, case, "bf16", n_splits=ns)
 
 
