@@ -37,21 +37,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATION_BYTES = 1 << 30
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_06_amd", "csrc", f)
-                  for f in ("fd_kernels.hip", "fd_mfma.hip", "fd_bifurcated.hip", "fd_device.h",
-                            "fd_internal.h", "fd_api.cpp")]
-
 WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_BIFURCATED)}
 DEFAULT_WORKLOAD = configs.CODELLAMA34B_SHARE.name
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        if os.path.exists(path):
-            with open(path, "rb") as f:
-                h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -264,15 +251,24 @@ def cpu_baseline(w, host_inputs, kv_bytes, budget_s):
     }
 
 
-def counters_for(kernel, workload):
+def counters_for(kernel, workload, n_splits):
     """HBM traffic per launch from committed rocprofv3 counter runs, or None
-    when the kernel sources changed since the counters were taken."""
+    when the kernel's sources (or its split count) changed since then."""
     try:
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
     entry = rec.get("entries", {}).get(f"{kernel}|{workload}")
-    if not entry or rec.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("n_splits") != n_splits:
+        return None
+    h = hashlib.sha256()
+    for rel in entry.get("sources", []):
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    if h.hexdigest()[:16] != entry.get("source_hash"):
         return None
     return entry.get("traffic_bytes")
 
@@ -287,14 +283,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
 
-    if args.print_source_hash:
-        print(kernel_source_hash())
-        return 0
     if args.calibrate_copy:
         import torch
 
@@ -370,7 +362,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": counters_for(info["kernel"], w.name),
+            "traffic": counters_for(info["kernel"], w.name, info["n_splits"]),
             "kernel_us": round(info["kernel_ms"] * 1e3, 3),
             "read_probe_gbs": None if info["probe_gbs"] is None else round(info["probe_gbs"], 1),
         },
