@@ -123,11 +123,33 @@ hipError_t launch_partial(const fd::PartialParams& p, const Path& path, int32_t 
     return path.mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, dtype, D, path.rows_per_block, s);
 }
 
-// Pieces for the context and for the decode part of a bifurcated call.
-void plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld,
-                     int32_t dtype, int32_t n_cu, int32_t* pc, int32_t* pd) {
-    *pc = fd_plan_splits(S, Hq, Hkv, D, Lc, dtype, n_cu);
-    *pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
+constexpr int64_t kMinContextPiece = 512;   // shortest context piece planned
+
+// Pieces for the context and for the decode part of a bifurcated call.  The
+// matrix-core context kernel (bf16, D 128) works on tiles of query rows;
+// its piece count fills about two workgroups per CU.  Otherwise the context
+// goes through the split-KV kernel like a batch of S sequences.
+struct BifPlan {
+    bool mfma_ctx;
+    int32_t row_tiles;
+    int32_t pc, pd;
+};
+
+BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld,
+                        int32_t dtype, int32_t n_cu) {
+    BifPlan b{};
+    b.mfma_ctx = dtype == FD_BF16 && D == 128;
+    if (b.mfma_ctx) {
+        b.row_tiles = fd::bif_context_row_tiles(S, Hq / Hkv);
+        const int64_t units = int64_t(Hkv) * b.row_tiles;
+        int64_t pc = (int64_t(n_cu) * kWgPerCu + units - 1) / units;
+        pc = std::min<int64_t>(pc, std::max<int64_t>(1, Lc / kMinContextPiece));
+        b.pc = int32_t(std::max<int64_t>(1, std::min<int64_t>(pc, FD_MAX_SPLITS)));
+    } else {
+        b.pc = fd_plan_splits(S, Hq, Hkv, D, Lc, dtype, n_cu);
+    }
+    b.pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
+    return b;
 }
 
 }  // namespace
@@ -343,9 +365,8 @@ fd_status fd_bifurcated_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
     FD_TRY(check_bifurcated_shapes(S, Hq, Hkv, D, Lc, Ld, dtype));
     int32_t cus = 0;
     FD_TRY(fd_device_cu_count(&cus));
-    int32_t pc = 0, pd = 0;
-    plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus, &pc, &pd);
-    *bytes = partial_layout(int64_t(S) * Hq, pc + pd, D).total();
+    const BifPlan plan = plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus);
+    *bytes = partial_layout(int64_t(S) * Hq, plan.pc + plan.pd, D).total();
     return FD_OK;
 }
 
@@ -370,8 +391,8 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
 
     int32_t cus = 0;
     FD_TRY(fd_device_cu_count(&cus));
-    int32_t pc = 0, pd = 0;
-    plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus, &pc, &pd);
+    const BifPlan plan = plan_bifurcated(S, Hq, Hkv, D, Lc, Ld, dtype, cus);
+    const int32_t pc = plan.pc, pd = plan.pd;
     const int32_t P = pc + pd;
     if (P > FD_MAX_PARTS) return fail(FD_ERR_UNSUPPORTED, "%d pieces exceed the combine limit %d", P, FD_MAX_PARTS);
     const int64_t rows = int64_t(S) * Hq;
@@ -384,29 +405,52 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     const Path path = choose_path(dtype, D, Hq / Hkv);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // Context part: every sample reads the same [Hkv, Lc, D] rows (batch
-    // stride 0); all Lc rows are valid.
     fd::PartialParams p{};
     p.q = q;
-    p.k = k_ctx;
-    p.v = v_ctx;
-    p.lens = nullptr;
     p.o_part = o_part;
     p.lse_part = lse_part;
-    p.Lmax = Lc;
-    p.kv_stride_b = 0;
-    p.kv_stride_h = Lc * D;
     p.B = S;
     p.Hq = Hq;
     p.Hkv = Hkv;
-    p.n_splits = pc;
     p.row_blocks = path.row_blocks;
     p.part_stride = P;
-    p.part_offset = 0;
     p.scale_log2 = resolve_scale(scale, D) * kLog2e;
     p.direct = 0;
-    hipError_t e = launch_partial(p, path, dtype, D, s);
-    if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+    hipError_t e;
+    if (plan.mfma_ctx) {
+        // Context part on the matrix cores: every KV head's context rows are
+        // read once per tile of query rows (samples x heads of the group).
+        fd::BifContextParams c{};
+        c.q = q;
+        c.k_ctx = k_ctx;
+        c.v_ctx = v_ctx;
+        c.o_part = o_part;
+        c.lse_part = lse_part;
+        c.S = S;
+        c.Hq = Hq;
+        c.Hkv = Hkv;
+        c.Lc = int32_t(Lc);
+        c.n_pieces = pc;
+        c.row_tiles = plan.row_tiles;
+        c.part_stride = P;
+        c.part_offset = 0;
+        c.scale_log2 = p.scale_log2;
+        e = fd::launch_bif_context(c, s);
+        if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+    } else {
+        // Context part through the split-KV kernel: every sample reads the
+        // same [Hkv, Lc, D] rows (batch stride 0); all Lc rows are valid.
+        p.k = k_ctx;
+        p.v = v_ctx;
+        p.lens = nullptr;
+        p.Lmax = Lc;
+        p.kv_stride_b = 0;
+        p.kv_stride_h = Lc * D;
+        p.n_splits = pc;
+        p.part_offset = 0;
+        e = launch_partial(p, path, dtype, D, s);
+        if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+    }
 
     // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
     p.k = k_dec;

@@ -36,6 +36,26 @@ struct PartialParams {
     int32_t direct;         // 1: n_splits == 1, write the final output
 };
 
+// Context part of a bifurcated call on the matrix cores (bf16, head_dim
+// 128): the S * G query rows of each KV head against that head's context,
+// cut into n_pieces pieces; writes pieces [part_offset, part_offset +
+// n_pieces) of every row.
+struct BifContextParams {
+    const void* q;          // [S, Hq, D]
+    const void* k_ctx;      // [Hkv, Lc, D]
+    const void* v_ctx;
+    float* o_part;          // [S*Hq, part_stride, D]
+    float* lse_part;        // [S*Hq, part_stride]
+    int32_t S, Hq, Hkv, Lc;
+    int32_t n_pieces;       // context pieces
+    int32_t row_tiles;      // bif_context_row_tiles(S, G)
+    int32_t part_stride, part_offset;
+    float scale_log2;
+};
+
+int bif_context_row_tiles(int S, int G);
+hipError_t launch_bif_context(const BifContextParams& p, hipStream_t stream);
+
 // Query rows handled by one work unit of the vector-ALU partial kernel for a
 // GQA group of G query heads: the largest of 8, 4, 2, 1 that divides G.
 inline int valu_rows_per_block(int G) {

@@ -396,6 +396,65 @@ __global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* _
     }
 }
 
+// LSE combine for rows with at most 64 pieces (the bifurcated calls and
+// short splits): one wave per row.  Lane j holds piece j's lse; the row
+// maximum and the weight sum are butterfly reductions (every lane ends with
+// the same bits); piece weights reach all lanes through v_readlane, and lane
+// j accumulates columns j, j + 64, ... with up to 8 pieces' loads in flight.
+constexpr int CMBW_ROWS = 4;                    // rows (waves) per workgroup
+constexpr int CMBW_MAXV = 8;                    // columns per lane: D <= 512
+
+template <int NV>
+__global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const float* __restrict__ o_part,
+                                                                          const float* __restrict__ lse_part,
+                                                                          int32_t rows, int32_t n_parts, int32_t D,
+                                                                          void* out, int32_t out_bf16,
+                                                                          float* lse_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * CMBW_ROWS + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float li = (lane < n_parts) ? lse_part[row * n_parts + lane] : -INFINITY;
+    float M = li;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = (li == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2ef);
+    float Z = w;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
+
+    const float* base = o_part + row * (int64_t)n_parts * D;
+    float acc[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) acc[k] = 0.f;
+    for (int i0 = 0; i0 < n_parts; i0 += 8) {
+        float v[8][NV];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = min(i0 + u, n_parts - 1);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int d = lane + 64 * k;
+                v[u][k] = (d < D) ? base[(int64_t)i * D + d] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (i0 + u < n_parts) {
+                const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i0 + u));
+#pragma unroll
+                for (int k = 0; k < NV; ++k) acc[k] = fmaf(wf, v[u][k], acc[k]);
+            }
+        }
+    }
+    const float inv = (Z > 0.f) ? 1.f / Z : 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) store_out(out, row * D + d, acc[k] * inv, out_bf16);
+    }
+    if (lane == 0 && lse_out) lse_out[row] = (Z > 0.f) ? M + logf(Z) : -INFINITY;
+}
+
 // HBM read ceiling: each workgroup streams one contiguous chunk of the
 // buffer with 16-byte loads, eight in flight per thread, and folds the data
 // into a word so the loads cannot be dropped.
@@ -460,6 +519,19 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                               int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
                               float* lse_out, hipStream_t stream) {
+    if (n_parts <= 64) {
+        const dim3 grid((unsigned)((rows + CMBW_ROWS - 1) / CMBW_ROWS));
+        const dim3 block(64 * CMBW_ROWS);
+        const int nv = (head_dim + 63) / 64;
+#define FD_CMBW(NV_) hipLaunchKernelGGL(lse_combine_rows_kernel<NV_>, grid, block, 0, stream, o_part, lse_part, \
+                                        rows, n_parts, head_dim, out, out_bf16, lse_out)
+        if (nv <= 1) FD_CMBW(1);
+        else if (nv == 2) FD_CMBW(2);
+        else if (nv <= 4) FD_CMBW(4);
+        else FD_CMBW(CMBW_MAXV);
+#undef FD_CMBW
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
     const bool vec4 = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(o_part) % 16 == 0);
     if (vec4)

@@ -31,44 +31,10 @@
 
 #include "fd_device.h"
 #include "fd_internal.h"
+#include "fd_mfma_common.h"
 
 namespace fd {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int MF_D = 128;
-constexpr int MF_TILE = 32;   // tokens per wave tile
-constexpr int MF_NW = 4;      // waves per workgroup
-
-__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Column e of the 8x8 bf16 block r[0..7] (row j = r[j], 8 elements each):
-// {r[0][e], r[1][e], ..., r[7][e]}, packed two per dword.
-template <int E>
-__device__ __forceinline__ u32x4_t block_column(const u32x4_t (&r)[8]) {
-    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-    constexpr int dw = E >> 1;
-    u32x4_t c;
-    c[0] = __builtin_amdgcn_perm(r[1][dw], r[0][dw], sel);
-    c[1] = __builtin_amdgcn_perm(r[3][dw], r[2][dw], sel);
-    c[2] = __builtin_amdgcn_perm(r[5][dw], r[4][dw], sel);
-    c[3] = __builtin_amdgcn_perm(r[7][dw], r[6][dw], sel);
-    return c;
-}
-
-template <int E, int NRB>
-__device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t (&pb)[NRB],
-                                         f32x4_t (&acc)[NRB][8]) {
-    const bf16x8_t va = as_bf16x8(block_column<E>(vr));
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], acc[r][E], 0, 0, 0);
-}
 
 // Loads one 32-token tile starting at row tb (tb < t1): K in score
 // A-operand layout, V as this lane's 8x8 block (rows 8g .. 8g+7, columns
@@ -90,66 +56,6 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
         const int t = min(tb + 8 * g + j, last);
         vr[j] = ld16(vbase + (int64_t)t * MF_D + 8 * i);
     }
-}
-
-// One tile of the online softmax: scores on the matrix cores, running max /
-// running sum update per query row, then O^T += V^T P^T.
-template <int NRB>
-__device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
-                                             const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
-                                             float (&m)[NRB], float (&l)[NRB], f32x4_t (&acc)[NRB][8]) {
-    const bool full = tb + MF_TILE <= t1;
-    bf16x8_t pb[NRB];
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        f32x4_t sc[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[blk], 0, 0, 0);
-        }
-        // Scores of this lane's query row for tokens tb + 8g + j, log2 domain.
-        float t[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            t[j] = sc[j >> 2][j & 3] * sl2;
-            if (!full && tb + 8 * g + j >= t1) t[j] = -INFINITY;
-        }
-        float mx = t[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[r], mx);
-        const float ref = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m[r] - ref);
-        // Weights rounded to bf16 for the matrix product; the running sum
-        // adds the same rounded values, so numerator and denominator agree.
-        float lsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            bf16x2_t w2;
-            w2.x = (__bf16)fast_exp2(t[j] - ref);
-            w2.y = (__bf16)fast_exp2(t[j + 1] - ref);
-            pb[r][j] = w2.x;
-            pb[r][j + 1] = w2.y;
-            lsum += (float)w2.x + (float)w2.y;
-        }
-        l[r] = l[r] * alpha + lsum;
-        m[r] = mn;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-    }
-    pv_block<0>(vr, pb, acc);
-    pv_block<1>(vr, pb, acc);
-    pv_block<2>(vr, pb, acc);
-    pv_block<3>(vr, pb, acc);
-    pv_block<4>(vr, pb, acc);
-    pv_block<5>(vr, pb, acc);
-    pv_block<6>(vr, pb, acc);
-    pv_block<7>(vr, pb, acc);
 }
 
 // NRB blocks of 16 query rows per work unit share every K/V load.
@@ -202,12 +108,12 @@ __global__ __launch_bounds__(256, (NRB == 1) ? 2 : 1) void partial_mfma_kernel(c
     const int ktok0 = 8 * (i >> 2) + (i & 3);
     const float sl2 = p.scale_log2;
 
-    f32x4_t acc[NRB][8];
-    float m[NRB], l[NRB];
+    f32x4_t acc[NRB][8], lacc[NRB];
+    float m[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         m[r] = -INFINITY;
-        l[r] = 0.f;
+        lacc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -224,21 +130,19 @@ __global__ __launch_bounds__(256, (NRB == 1) ? 2 : 1) void partial_mfma_kernel(c
         load_tile(kbase, vbase, tb, t1, ktok0, g, i, ka, va);
         while (true) {
             load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, kb2, vb2);
-            compute_tile<NRB>(ka, va, qb, tb, t1, g, sl2, m, l, acc);
+            compute_tile<NRB>(ka, va, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;
             load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, ka, va);
-            compute_tile<NRB>(kb2, vb2, qb, tb, t1, g, sl2, m, l, acc);
+            compute_tile<NRB>(kb2, vb2, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;
         }
     }
 
-    // Row sums over the four lane groups, then hand the wave state to LDS.
+    // Hand the wave state (row sums already complete in lacc) to LDS.
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-        l[r] += __shfl_xor(l[r], 16);
-        l[r] += __shfl_xor(l[r], 32);
         const int row = r * 16 + i;
         if (row < nr) {
 #pragma unroll
@@ -247,7 +151,7 @@ __global__ __launch_bounds__(256, (NRB == 1) ? 2 : 1) void partial_mfma_kernel(c
                 for (int ii = 0; ii < 4; ++ii) s_acc[wave][row][8 * (4 * g + ii) + e] = acc[r][e][ii];
             if (g == 0) {
                 s_m[wave][row] = m[r];
-                s_l[wave][row] = l[r];
+                s_l[wave][row] = lacc[r][0];
             }
         }
     }

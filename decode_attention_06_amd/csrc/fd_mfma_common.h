@@ -1,0 +1,125 @@
+// Matrix-core helpers shared by the split-KV and bifurcated kernels
+// (gfx950, bf16, head_dim 128, v_mfma_f32_16x16x32_bf16).  Internal.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16,
+// i = l % 16): A holds row i, k = 8g .. 8g+7; B holds column i, the same k;
+// the f32x4 result holds rows 4g .. 4g+3 of column i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+
+namespace fd {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int MF_D = 128;
+constexpr int MF_TILE = 32;   // tokens per wave tile
+constexpr int MF_NW = 4;      // waves per workgroup (split-KV kernel)
+
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Column e of the 8x8 bf16 block r[0..7] (row j = r[j], 8 elements each):
+// {r[0][e], r[1][e], ..., r[7][e]}, packed two per dword.
+template <int E>
+__device__ __forceinline__ u32x4_t block_column(const u32x4_t (&r)[8]) {
+    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+    constexpr int dw = E >> 1;
+    u32x4_t c;
+    c[0] = __builtin_amdgcn_perm(r[1][dw], r[0][dw], sel);
+    c[1] = __builtin_amdgcn_perm(r[3][dw], r[2][dw], sel);
+    c[2] = __builtin_amdgcn_perm(r[5][dw], r[4][dw], sel);
+    c[3] = __builtin_amdgcn_perm(r[7][dw], r[6][dw], sel);
+    return c;
+}
+
+template <int E, int NRB>
+__device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t (&pb)[NRB],
+                                         f32x4_t (&acc)[NRB][8]) {
+    const bf16x8_t va = as_bf16x8(block_column<E>(vr));
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], acc[r][E], 0, 0, 0);
+}
+
+// One 32-token tile of the online softmax for NRB blocks of 16 query rows:
+// scores S^T = K Q^T on the matrix cores (K in kr: token block blk, k-step
+// s, lane (g, i) holds token 8*(i/4) + 4*blk + i%4, d = 32s + 8g .. +8),
+// running max per query row (m, log2 domain) and running sum (lacc: every
+// component holds the row's sum), then O^T += V^T P^T (V in vr: lane (g, i)
+// holds tokens 8g .. 8g+7, d = 8i .. 8i+7).  Tokens at or beyond t1 get
+// weight 0.
+template <int NRB>
+__device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
+                                             const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
+                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8]) {
+    const bool full = tb + MF_TILE <= t1;
+    // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
+    // the very weights used in P V, accumulated in fp32 by the matrix core.
+    const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    bf16x8_t pb[NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        f32x4_t sc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            sc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[blk], 0, 0, 0);
+        }
+        // Raw scores q.k of this lane's query row for tokens tb + 8g + j.
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            t[j] = sc[j >> 2][j & 3];
+            if (!full && tb + 8 * g + j >= t1) t[j] = -INFINITY;
+        }
+        float mx = t[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Running max in the log2 domain (scale * log2(e) folded in; sl2 > 0).
+        const float mn = fmaxf(m[r], mx * sl2);
+        const float ref = (mn == -INFINITY) ? 0.f : mn;
+        // Rescale only when some row of the wave raised its maximum; otherwise
+        // every factor would be exp2(0) = 1.
+        if (__any(mn > m[r])) {
+            const float alpha = fast_exp2(m[r] - ref);
+            lacc[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+        }
+        m[r] = mn;
+        // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix product.
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            bf16x2_t w2;
+            w2.x = (__bf16)fast_exp2(fmaf(t[j], sl2, -ref));
+            w2.y = (__bf16)fast_exp2(fmaf(t[j + 1], sl2, -ref));
+            pb[r][j] = w2.x;
+            pb[r][j + 1] = w2.y;
+        }
+        lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[r], lacc[r], 0, 0, 0);
+    }
+    pv_block<0>(vr, pb, acc);
+    pv_block<1>(vr, pb, acc);
+    pv_block<2>(vr, pb, acc);
+    pv_block<3>(vr, pb, acc);
+    pv_block<4>(vr, pb, acc);
+    pv_block<5>(vr, pb, acc);
+    pv_block<6>(vr, pb, acc);
+    pv_block<7>(vr, pb, acc);
+}
+
+}  // namespace
+}  // namespace fd

@@ -117,13 +117,15 @@ def test_bitwise_repeatable(fd):
 
 # ------------------------------------------------------------ combine op
 
-def test_lse_combine_matches_oracle(fd):
-    rng = np.random.Generator(np.random.PCG64(12))
-    rows, P, D = 37, 19, 128
+@pytest.mark.parametrize("rows,P,D", [(37, 19, 128), (5, 64, 128), (9, 65, 128), (4, 300, 128), (7, 3, 64),
+                                      (6, 40, 100), (3, 70, 100), (2, 1, 128), (3, 17, 512)])
+def test_lse_combine_matches_oracle(fd, rows, P, D):
+    # up to 64 pieces: one wave per row; more: the column-slice kernel
+    rng = np.random.Generator(np.random.PCG64(12 + P))
     o = rng.standard_normal((rows, P, D)).astype(np.float32)
     lse = (rng.standard_normal((rows, P)) * 5).astype(np.float32)
     empty = rng.random((rows, P)) < 0.3
-    empty[:, 3] = False                    # every row keeps one finite piece
+    empty[:, P // 2] = False               # every row keeps one finite piece
     lse[empty] = -np.inf
     o[np.isneginf(lse)] = 0.0
     out, l = fd.lse_combine(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(), return_lse=True)
