@@ -13,8 +13,9 @@
 //
 // Work unit: (KV head, context piece, tile of 32 * CTX_NW query rows).  The
 // query rows of a KV head are the (sample, head-in-group) pairs that read it,
-// S * G of them.  A workgroup stages 64-token K/V tiles in LDS (double
-// buffered, XOR-swizzled 16-byte chunks) and every wave contracts them
+// S * G of them.  A workgroup streams 32-token K/V tiles straight from global
+// memory into a ring of LDS stages (XOR-swizzled 16-byte chunks, three tiles
+// in flight) and every wave contracts them
 // against its own 32 rows with the same register layout as the split-KV
 // matrix-core kernel, so each wave owns its rows for the whole piece and no
 // cross-wave merge is needed.  Workgroup ids are arranged so that all row
@@ -32,47 +33,57 @@ namespace {
 
 constexpr int CTX_NW = 4;                 // waves per workgroup
 constexpr int CTX_ROWS = 32 * CTX_NW;     // query rows per workgroup
-constexpr int CTX_TILE = 64;              // tokens per LDS tile
+constexpr int CTX_TILE = MF_TILE;         // tokens per LDS tile (32)
+constexpr int CTX_STAGES = 4;             // LDS ring: three tiles in flight
+constexpr int CTX_TILE_BYTES = CTX_TILE * 256;
 constexpr int XCDS = 8;
 
-// LDS byte offset of 16-byte chunk c (0..15) of token row t in a tile.  The
-// chunk index is XORed with (t & 3) | (bit 3 of t) << 2, which makes the
-// K-operand reads (8 lanes: tokens {0..3, 8..11} + const, same chunk), the
-// V-block reads (8 lanes: one token, chunks 0..7) and the tile writes
-// (8 threads: one token, 8 consecutive chunks) hit 8 distinct bank groups.
-__device__ __forceinline__ int lds_off(int t, int c) {
-    const int f = (t & 3) | (((t >> 3) & 1) << 2);
-    return t * 256 + ((c ^ f) << 4);
-}
+// LDS byte offset of 16-byte chunk c (0..15) of token row t (0..31) in a
+// tile.  The chunk index is XORed with (t & 3) | (bits 3-4 of t) << 2, which
+// makes the K-operand reads (16 lanes: tokens {0..3, 8..11, 16..19, 24..27}
+// + const, one chunk) and the V-block reads (16 lanes: one token, chunks
+// 0..15) touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int t) { return (t & 3) | (((t >> 3) & 3) << 2); }
+__device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ swz(t)) << 4); }
 
-struct TileStage {
-    u32x4_t k[4], v[4];
-};
-
-// Global -> registers for one 64-token tile: thread th covers rows
-// th / 16 + 16u, chunk th % 16.  Rows at or beyond c1 clamp to c1 - 1.
-__device__ __forceinline__ void fetch_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1, int th,
-                                           TileStage& st) {
+// Issue the loads of one 32-token tile straight into LDS
+// (global_load_lds_dwordx4: lane L of a wave instruction lands at the
+// instruction's LDS base + 16 L).  Wave w fills K and V bytes
+// [2048 w, 2048 w + 2048) of the stage: rows 8w .. 8w+7; lane L of part k
+// writes row 8w + 4k + L/16 at chunk position L%16, so it fetches chunk
+// (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1.
+// Four vector-memory instructions per wave.
+__device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1,
+                                           int wave, int lane, char* kst, char* vst) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int t = min(t0 + th / 16 + 16 * u, c1 - 1);
-        st.k[u] = ld16(kbase + (int64_t)t * MF_D + 8 * (th % 16));
-        st.v[u] = ld16(vbase + (int64_t)t * MF_D + 8 * (th % 16));
+    for (int k = 0; k < 2; ++k) {
+        const int row = 8 * wave + 4 * k + (lane >> 4);
+        const int chunk = (lane & 15) ^ swz(row);
+        const int t = min(t0 + row, c1 - 1);
+        const int base = 1024 * (2 * wave + k);
+        __builtin_amdgcn_global_load_lds(kbase + (int64_t)t * MF_D + 8 * chunk, (lds_ptr)(kst + base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + (int64_t)t * MF_D + 8 * chunk, (lds_ptr)(vst + base), 16, 0, 0);
     }
 }
 
-__device__ __forceinline__ void store_tile(char* kl, char* vl, int th, const TileStage& st) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int off = lds_off(th / 16 + 16 * u, th % 16);
-        *reinterpret_cast<u32x4_t*>(kl + off) = st.k[u];
-        *reinterpret_cast<u32x4_t*>(vl + off) = st.v[u];
-    }
+// s_waitcnt with only the vector-memory count constrained (expcnt and
+// lgkmcnt at their maxima): wait until at most N loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __global__ __launch_bounds__(64 * CTX_NW, 2) void bif_context_kernel(const BifContextParams p) {
-    __shared__ __attribute__((aligned(16))) char s_k[2][CTX_TILE * 256];
-    __shared__ __attribute__((aligned(16))) char s_v[2][CTX_TILE * 256];
+    // One LDS object per stage and per operand, addressed with constant stage
+    // numbers only, so the compiler can tell the tile being read from the
+    // tiles still being written by in-flight loads.
+    __shared__ __attribute__((aligned(16))) char s_k0[CTX_TILE_BYTES], s_k1[CTX_TILE_BYTES],
+        s_k2[CTX_TILE_BYTES], s_k3[CTX_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s_v0[CTX_TILE_BYTES], s_v1[CTX_TILE_BYTES],
+        s_v2[CTX_TILE_BYTES], s_v3[CTX_TILE_BYTES];
+    char* const ks[CTX_STAGES] = {s_k0, s_k1, s_k2, s_k3};
+    char* const vs[CTX_STAGES] = {s_v0, s_v1, s_v2, s_v3};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -128,34 +139,46 @@ __global__ __launch_bounds__(64 * CTX_NW, 2) void bif_context_kernel(const BifCo
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (c0 < c1) {
-        TileStage st;
-        fetch_tile(kbase, vbase, c0, c1, tid, st);
-        store_tile(s_k[0], s_v[0], tid, st);
-        __syncthreads();
-        int buf = 0;
-        for (int t0 = c0; t0 < c1; t0 += CTX_TILE) {
-            const bool more = t0 + CTX_TILE < c1;
-            if (more) fetch_tile(kbase, vbase, t0 + CTX_TILE, c1, tid, st);
-            const char* kl = s_k[buf];
-            const char* vl = s_v[buf];
+    // Ring of CTX_STAGES LDS tiles: tile t lives in stage t % CTX_STAGES and
+    // its loads are issued three tiles ahead.  Before tile t is used, each
+    // wave waits for its own loads of tile t (the later tiles' loads may
+    // stay in flight) and the barrier makes every wave's part visible; the
+    // same barrier tells that all waves are done with tile t - 1, whose
+    // stage the loads of tile t + 3 then overwrite.
+    const int n_tiles = (c1 - c0 + CTX_TILE - 1) / CTX_TILE;
 #pragma unroll
-            for (int sub = 0; sub < CTX_TILE / MF_TILE; ++sub) {
+    for (int t = 0; t < CTX_STAGES - 1; ++t)
+        if (t < n_tiles) issue_tile(kbase, vbase, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
+    for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
+#pragma unroll
+        for (int st = 0; st < CTX_STAGES; ++st) {
+            const int t = t4 + st;
+            if (t < n_tiles) {
+                if (t + 2 < n_tiles)
+                    wait_vm<8>();
+                else if (t + 1 < n_tiles)
+                    wait_vm<4>();
+                else
+                    wait_vm<0>();
+                __syncthreads();
+                if (t + CTX_STAGES - 1 < n_tiles) {
+                    const int nst = (st + CTX_STAGES - 1) % CTX_STAGES;
+                    issue_tile(kbase, vbase, c0 + (t + CTX_STAGES - 1) * CTX_TILE, c1, wave, lane, ks[nst], vs[nst]);
+                }
+                const char* kl = ks[st];
+                const char* vl = vs[st];
                 u32x4_t kr[2][4], vr[8];
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
-                    const int t = sub * MF_TILE + ktok0 + 4 * blk;
+                    const int tt = ktok0 + 4 * blk;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4_t*>(kl + lds_off(t, 4 * s + g));
+                    for (int s = 0; s < 4; ++s)
+                        kr[blk][s] = *reinterpret_cast<const u32x4_t*>(kl + lds_off(tt, 4 * s + g));
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    vr[j] = *reinterpret_cast<const u32x4_t*>(vl + lds_off(sub * MF_TILE + 8 * g + j, i));
-                compute_tile<2>(kr, vr, qb, t0 + sub * MF_TILE, c1, g, sl2, m, lacc, acc);
+                for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const u32x4_t*>(vl + lds_off(8 * g + j, i));
+                compute_tile<2>(kr, vr, qb, c0 + t * CTX_TILE, c1, g, sl2, m, lacc, acc);
             }
-            if (more) store_tile(s_k[buf ^ 1], s_v[buf ^ 1], tid, st);
-            __syncthreads();
-            buf ^= 1;
         }
     }
 

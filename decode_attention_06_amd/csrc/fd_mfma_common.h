@@ -57,6 +57,13 @@ __device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t 
 // component holds the row's sum), then O^T += V^T P^T (V in vr: lane (g, i)
 // holds tokens 8g .. 8g+7, d = 8i .. 8i+7).  Tokens at or beyond t1 get
 // weight 0.
+// The running maximum m is a reference, not necessarily the exact maximum:
+// it is raised only when a score exceeds it by more than MF_RESCALE_SLACK
+// (log2 units), so weights stay below 2^MF_RESCALE_SLACK and the costly
+// rescale of the accumulators is skipped for almost every tile.  Output
+// (acc / l) and lse (m + log2 l) do not depend on the reference chosen.
+constexpr float MF_RESCALE_SLACK = 8.0f;
+
 template <int NRB>
 __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
                                              const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
@@ -86,20 +93,21 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
         float mx = t[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Running max in the log2 domain (scale * log2(e) folded in; sl2 > 0).
-        const float mn = fmaxf(m[r], mx * sl2);
-        const float ref = (mn == -INFINITY) ? 0.f : mn;
-        // Rescale only when some row of the wave raised its maximum; otherwise
-        // every factor would be exp2(0) = 1.
-        if (__any(mn > m[r])) {
-            const float alpha = fast_exp2(m[r] - ref);
+        // Reference in the log2 domain (scale * log2(e) folded in; sl2 > 0).
+        // Only when one of this lane's scores passes the reference by more
+        // than the slack is the row maximum over the four lane groups formed
+        // and the reference raised, identically in all lanes of the row.
+        if (__any(mx * sl2 > m[r] + MF_RESCALE_SLACK)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m[r], mx * sl2);
+            const float alpha = fast_exp2(m[r] - ((mn == -INFINITY) ? 0.f : mn));
             lacc[r] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+            m[r] = mn;
         }
-        m[r] = mn;
+        const float ref = (m[r] == -INFINITY) ? 0.f : m[r];
         // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix product.
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
