@@ -33,7 +33,8 @@ fd_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int32_t kWgPerCu = 2;        // partial-kernel workgroups to keep per CU
-constexpr int64_t kMinChunk = 256;     // shortest piece worth a partial result
+constexpr int64_t kMinChunk = 256;     // shortest piece worth a partial result (vector-ALU kernel)
+constexpr int64_t kMinChunkMfma = 128; // matrix-core kernel: one 32-token tile per wave
 constexpr int64_t kMaxLen = int64_t(1) << 30;
 constexpr size_t kAlign = 256;
 
@@ -123,7 +124,7 @@ hipError_t launch_partial(const fd::PartialParams& p, const Path& path, int32_t 
     return path.mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, dtype, D, path.rows_per_block, s);
 }
 
-constexpr int64_t kMinContextPiece = 512;   // shortest context piece planned
+constexpr int64_t kMinContextPiece = 256;   // shortest context piece planned
 
 // Pieces for the context and for the decode part of a bifurcated call.  The
 // matrix-core context kernel (bf16, D 128) works on tiles of query rows;
@@ -142,7 +143,8 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
     if (b.mfma_ctx) {
         b.row_tiles = fd::bif_context_row_tiles(S, Hq / Hkv);
         const int64_t units = int64_t(Hkv) * b.row_tiles;
-        int64_t pc = (int64_t(n_cu) * kWgPerCu + units - 1) / units;
+        const int64_t wg_per_cu = fd::bif_context_waves(S, Hq / Hkv) == 8 ? 1 : kWgPerCu;
+        int64_t pc = (int64_t(n_cu) * wg_per_cu + units - 1) / units;
         pc = std::min<int64_t>(pc, std::max<int64_t>(1, Lc / kMinContextPiece));
         b.pc = int32_t(std::max<int64_t>(1, std::min<int64_t>(pc, FD_MAX_SPLITS)));
     } else {
@@ -177,11 +179,12 @@ int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
         n_cu <= 0 || num_q_heads % num_kv_heads != 0 || (dtype != FD_F32 && dtype != FD_BF16))
         return -1;
     const int G = num_q_heads / num_kv_heads;
-    const int64_t units = int64_t(batch) * num_kv_heads * choose_path(dtype, head_dim, G).row_blocks;
+    const Path path = choose_path(dtype, head_dim, G);
+    const int64_t units = int64_t(batch) * num_kv_heads * path.row_blocks;
     const int64_t target = int64_t(n_cu) * kWgPerCu;
     if (units >= target) return 1;
     int64_t s = (target + units - 1) / units;
-    const int64_t by_len = std::max<int64_t>(1, max_len / kMinChunk);
+    const int64_t by_len = std::max<int64_t>(1, max_len / (path.mfma ? kMinChunkMfma : kMinChunk));
     s = std::min<int64_t>(s, by_len);
     s = std::min<int64_t>(s, FD_MAX_SPLITS);
     return int32_t(std::max<int64_t>(s, 1));

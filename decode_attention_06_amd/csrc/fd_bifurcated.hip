@@ -11,7 +11,8 @@
 // decodificación necesita otra planificación") whose partial outputs and
 // log-sum-exps join the decode pieces in the LSE combine.
 //
-// Work unit: (KV head, context piece, tile of 32 * CTX_NW query rows).  The
+// Work unit: (KV head, context piece, tile of 32 * NW query rows, NW = 4
+// or 8 waves).  The
 // query rows of a KV head are the (sample, head-in-group) pairs that read it,
 // S * G of them.  A workgroup streams 32-token K/V tiles straight from global
 // memory into a ring of LDS stages (XOR-swizzled 16-byte chunks, three tiles
@@ -31,8 +32,6 @@
 namespace fd {
 namespace {
 
-constexpr int CTX_NW = 4;                 // waves per workgroup
-constexpr int CTX_ROWS = 32 * CTX_NW;     // query rows per workgroup
 constexpr int CTX_TILE = MF_TILE;         // tokens per LDS tile (32)
 constexpr int CTX_STAGES = 4;             // LDS ring: three tiles in flight
 constexpr int CTX_TILE_BYTES = CTX_TILE * 256;
@@ -51,20 +50,66 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ sw
 // instruction's LDS base + 16 L).  Wave w fills K and V bytes
 // [2048 w, 2048 w + 2048) of the stage: rows 8w .. 8w+7; lane L of part k
 // writes row 8w + 4k + L/16 at chunk position L%16, so it fetches chunk
-// (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1.
+// (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1
+// (c1 > t0 is not required: a tile past the end re-reads row c1 - 1).
 // Four vector-memory instructions per wave.
-__device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1,
-                                           int wave, int lane, char* kst, char* vst) {
+// Address registers of one wave's loads for a tile (2 per KiB per operand;
+// 4 waves use all four, 8 waves the first two).
+struct TileAddrs {
+    const uint16_t* p[4];
+};
+
+template <int NW>
+__device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1,
+                                                    int wave, int lane, char* kst, char* vst) {
     typedef __attribute__((address_space(3))) void* lds_ptr;
+    constexpr int IPW = 8 / NW;             // 1 KiB loads per wave per operand
+    TileAddrs a;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int row = 8 * wave + 4 * k + (lane >> 4);
+    for (int k = 0; k < IPW; ++k) {
+        const int row = 4 * IPW * wave + 4 * k + (lane >> 4);
         const int chunk = (lane & 15) ^ swz(row);
         const int t = min(t0 + row, c1 - 1);
-        const int base = 1024 * (2 * wave + k);
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)t * MF_D + 8 * chunk, (lds_ptr)(kst + base), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + (int64_t)t * MF_D + 8 * chunk, (lds_ptr)(vst + base), 16, 0, 0);
+        const int base = 1024 * (IPW * wave + k);
+        a.p[2 * k] = kbase + (int64_t)t * MF_D + 8 * chunk;
+        a.p[2 * k + 1] = vbase + (int64_t)t * MF_D + 8 * chunk;
+        __builtin_amdgcn_global_load_lds(a.p[2 * k], (lds_ptr)(kst + base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.p[2 * k + 1], (lds_ptr)(vst + base), 16, 0, 0);
     }
+    return a;
+}
+
+// Keeps the address registers of the last issued tile alive up to this
+// point (no instruction is emitted), so the registers of the LDS reads that
+// follow the issue are never the in-flight loads' address registers and the
+// compiler needs no wait for them.
+template <int NW>
+__device__ __forceinline__ void keep_addrs(const TileAddrs& a) {
+    if constexpr (NW == 4)
+        asm volatile("" ::"v"(a.p[0]), "v"(a.p[1]), "v"(a.p[2]), "v"(a.p[3]));
+    else
+        asm volatile("" ::"v"(a.p[0]), "v"(a.p[1]));
+}
+
+// One ring step: issue the loads of a later tile into stage (wk, wv) and
+// read the next tile's operands from stage (rk, rv).  The restrict
+// qualifiers state that the stages are disjoint, which lets the compiler
+// read one stage while the other is still being filled.
+template <int NW>
+__device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint16_t* vbase, int t_issue, int c1,
+                                                   int wave, int lane, char* __restrict__ wk, char* __restrict__ wv,
+                                                   const char* __restrict__ rk, const char* __restrict__ rv, int ktok0,
+                                                   int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
+    const TileAddrs a = issue_tile<NW>(kbase, vbase, t_issue, c1, wave, lane, wk, wv);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int tt = ktok0 + 4 * blk;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4_t*>(rk + lds_off(tt, 4 * s + g));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const u32x4_t*>(rv + lds_off(8 * g + j, i));
+    return a;
 }
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and
@@ -74,16 +119,27 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__global__ __launch_bounds__(64 * CTX_NW, 2) void bif_context_kernel(const BifContextParams p) {
-    // One LDS object per stage and per operand, addressed with constant stage
-    // numbers only, so the compiler can tell the tile being read from the
-    // tiles still being written by in-flight loads.
-    __shared__ __attribute__((aligned(16))) char s_k0[CTX_TILE_BYTES], s_k1[CTX_TILE_BYTES],
-        s_k2[CTX_TILE_BYTES], s_k3[CTX_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s_v0[CTX_TILE_BYTES], s_v1[CTX_TILE_BYTES],
-        s_v2[CTX_TILE_BYTES], s_v3[CTX_TILE_BYTES];
-    char* const ks[CTX_STAGES] = {s_k0, s_k1, s_k2, s_k3};
-    char* const vs[CTX_STAGES] = {s_v0, s_v1, s_v2, s_v3};
+// Workgroup barrier without the fence __syncthreads() carries: that fence
+// waits for every outstanding vector-memory load, the tiles still in flight
+// included.  The ring needs no more than the barrier itself: each wave has
+// waited for its own loads of the tile about to be read (wait_vm) and has
+// consumed its LDS reads of the tile whose stage is refilled next.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 4) ? 2 : 1) void bif_context_kernel(const BifContextParams p) {
+    constexpr int CTX_ROWS = 32 * NW;
+    // Loads outstanding per wave for two tiles.
+    constexpr int TWO_TILES = 2 * 2 * (8 / NW);
+    // One LDS object per stage (K tile, then V tile), addressed with constant
+    // stage numbers only, so the compiler can tell the tile being read from
+    // the tiles still being written by in-flight loads.
+    __shared__ __attribute__((aligned(16))) char s_t0[2 * CTX_TILE_BYTES], s_t1[2 * CTX_TILE_BYTES],
+        s_t2[2 * CTX_TILE_BYTES], s_t3[2 * CTX_TILE_BYTES];
+    char* const ks[CTX_STAGES] = {s_t0, s_t1, s_t2, s_t3};
+    char* const vs[CTX_STAGES] = {s_t0 + CTX_TILE_BYTES, s_t1 + CTX_TILE_BYTES, s_t2 + CTX_TILE_BYTES,
+                                  s_t3 + CTX_TILE_BYTES};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -139,47 +195,45 @@ __global__ __launch_bounds__(64 * CTX_NW, 2) void bif_context_kernel(const BifCo
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Ring of CTX_STAGES LDS tiles: tile t lives in stage t % CTX_STAGES and
-    // its loads are issued three tiles ahead.  Before tile t is used, each
-    // wave waits for its own loads of tile t (the later tiles' loads may
-    // stay in flight) and the barrier makes every wave's part visible; the
-    // same barrier tells that all waves are done with tile t - 1, whose
-    // stage the loads of tile t + 3 then overwrite.
-    const int n_tiles = (c1 - c0 + CTX_TILE - 1) / CTX_TILE;
+    // Ring of CTX_STAGES LDS tiles: tile t lives in stage t % CTX_STAGES.
+    // Every step issues exactly four loads per wave (tiles past the end
+    // re-read the piece's last row into a stage nobody reads again), so
+    // the wait for all but two tiles' loads before reading tile t + 1 leaves it complete on every path
+    // (tiles t + 2 and t + 3 may stay in flight); the barrier after it makes
+    // all waves' parts visible and tells that all waves are done with tile
+    // t, whose stage the loads of tile t + 4 then refill.  The LDS reads of
+    // the next tile sit at the end of each step, after that step's issue, so
+    // the compiler sees which stages are still being filled.
+    if (c0 < c1) {
+        const int n_tiles = (c1 - c0 + CTX_TILE - 1) / CTX_TILE;
+        // The query fragments are in registers before the ring starts, so the
+        // waits below count tile loads only.
+        wait_vm<0>();
+        u32x4_t kr[2][4], vr[8];
 #pragma unroll
-    for (int t = 0; t < CTX_STAGES - 1; ++t)
-        if (t < n_tiles) issue_tile(kbase, vbase, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
-    for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
+        for (int t = 0; t < CTX_STAGES - 1; ++t)
+            issue_tile<NW>(kbase, vbase, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
+        wait_vm<TWO_TILES>();
+        ring_barrier();
+        const TileAddrs a0 = ring_step<NW>(kbase, vbase, c0 + (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
+                                       ks[CTX_STAGES - 1], vs[CTX_STAGES - 1], ks[0], vs[0], ktok0, g, i, kr, vr);
+        keep_addrs<NW>(a0);
+        for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
 #pragma unroll
-        for (int st = 0; st < CTX_STAGES; ++st) {
-            const int t = t4 + st;
-            if (t < n_tiles) {
-                if (t + 2 < n_tiles)
-                    wait_vm<8>();
-                else if (t + 1 < n_tiles)
-                    wait_vm<4>();
-                else
-                    wait_vm<0>();
-                __syncthreads();
-                if (t + CTX_STAGES - 1 < n_tiles) {
-                    const int nst = (st + CTX_STAGES - 1) % CTX_STAGES;
-                    issue_tile(kbase, vbase, c0 + (t + CTX_STAGES - 1) * CTX_TILE, c1, wave, lane, ks[nst], vs[nst]);
-                }
-                const char* kl = ks[st];
-                const char* vl = vs[st];
-                u32x4_t kr[2][4], vr[8];
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
-                    const int tt = ktok0 + 4 * blk;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        kr[blk][s] = *reinterpret_cast<const u32x4_t*>(kl + lds_off(tt, 4 * s + g));
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const u32x4_t*>(vl + lds_off(8 * g + j, i));
+            for (int st = 0; st < CTX_STAGES; ++st) {
+                const int t = t4 + st;
                 compute_tile<2>(kr, vr, qb, c0 + t * CTX_TILE, c1, g, sl2, m, lacc, acc);
+                if (t + 1 >= n_tiles) break;
+                wait_vm<TWO_TILES>();
+                ring_barrier();
+                const TileAddrs an = ring_step<NW>(kbase, vbase, c0 + (t + CTX_STAGES) * CTX_TILE, c1, wave, lane,
+                                               ks[st], vs[st], ks[(st + 1) % CTX_STAGES], vs[(st + 1) % CTX_STAGES],
+                                               ktok0, g, i, kr, vr);
+                keep_addrs<NW>(an);
             }
         }
+        // No load into this workgroup's LDS may outlive it.
+        wait_vm<0>();
     }
 
     // Each wave owns its rows (sums complete in lacc): write this piece.
@@ -210,12 +264,20 @@ __global__ __launch_bounds__(64 * CTX_NW, 2) void bif_context_kernel(const BifCo
 
 }  // namespace
 
-int bif_context_row_tiles(int S, int G) { return (S * G + CTX_ROWS - 1) / CTX_ROWS; }
+int bif_context_waves(int, int) { return 4; }
+
+int bif_context_row_tiles(int S, int G) {
+    const int rows = 32 * bif_context_waves(S, G);
+    return (S * G + rows - 1) / rows;
+}
 
 hipError_t launch_bif_context(const BifContextParams& p, hipStream_t stream) {
     const int units = p.Hkv * p.n_pieces;
     const int64_t wgs = (int64_t)((units + XCDS - 1) / XCDS) * XCDS * p.row_tiles;
-    hipLaunchKernelGGL(bif_context_kernel, dim3((unsigned)wgs), dim3(64 * CTX_NW), 0, stream, p);
+    if (bif_context_waves(p.S, p.Hq / p.Hkv) == 8)
+        hipLaunchKernelGGL(bif_context_kernel<8>, dim3((unsigned)wgs), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL(bif_context_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct BifContextParams {
     float scale_log2;
 };
 
+int bif_context_waves(int S, int G);        // 8 (one workgroup per CU) or 4
 int bif_context_row_tiles(int S, int G);
 hipError_t launch_bif_context(const BifContextParams& p, hipStream_t stream);
 

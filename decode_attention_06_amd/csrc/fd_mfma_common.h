@@ -72,48 +72,60 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
     // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
     // the very weights used in P V, accumulated in fp32 by the matrix core.
     const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    bf16x8_t pb[NRB];
+    // All score products first (independent chains for the scheduler).
+    f32x4_t sc[NRB][2];
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        f32x4_t sc[2];
+    for (int r = 0; r < NRB; ++r)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            sc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sc[r][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[blk], 0, 0, 0);
+                sc[r][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[r][blk], 0, 0, 0);
         }
-        // Raw scores q.k of this lane's query row for tokens tb + 8g + j.
-        float t[8];
+    // Raw scores q.k of this lane's query rows for tokens tb + 8g + j, and
+    // this lane's maximum per row block.
+    float t[NRB][8], mx[NRB];
+    bool raise = false;
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            t[j] = sc[j >> 2][j & 3];
-            if (!full && tb + 8 * g + j >= t1) t[j] = -INFINITY;
+            t[r][j] = sc[r][j >> 2][j & 3];
+            if (!full && tb + 8 * g + j >= t1) t[r][j] = -INFINITY;
         }
-        float mx = t[0];
+        mx[r] = t[r][0];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
+        for (int j = 1; j < 8; ++j) mx[r] = fmaxf(mx[r], t[r][j]);
         // Reference in the log2 domain (scale * log2(e) folded in; sl2 > 0).
-        // Only when one of this lane's scores passes the reference by more
-        // than the slack is the row maximum over the four lane groups formed
-        // and the reference raised, identically in all lanes of the row.
-        if (__any(mx * sl2 > m[r] + MF_RESCALE_SLACK)) {
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m[r], mx * sl2);
+        raise = raise || (mx[r] * sl2 > m[r] + MF_RESCALE_SLACK);
+    }
+    // Rare path: some score passed its row's reference by more than the
+    // slack.  Form the row maxima over the four lane groups and raise every
+    // row's reference, identically in all lanes of the row.
+    if (__any(raise)) {
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            float x = fmaxf(mx[r], __shfl_xor(mx[r], 16));
+            x = fmaxf(x, __shfl_xor(x, 32));
+            const float mn = fmaxf(m[r], x * sl2);
             const float alpha = fast_exp2(m[r] - ((mn == -INFINITY) ? 0.f : mn));
             lacc[r] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
             m[r] = mn;
         }
+    }
+    // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix products.
+    bf16x8_t pb[NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
         const float ref = (m[r] == -INFINITY) ? 0.f : m[r];
-        // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix product.
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
             bf16x2_t w2;
-            w2.x = (__bf16)fast_exp2(fmaf(t[j], sl2, -ref));
-            w2.y = (__bf16)fast_exp2(fmaf(t[j + 1], sl2, -ref));
+            w2.x = (__bf16)fast_exp2(fmaf(t[r][j], sl2, -ref));
+            w2.y = (__bf16)fast_exp2(fmaf(t[r][j + 1], sl2, -ref));
             pb[r][j] = w2.x;
             pb[r][j + 1] = w2.y;
         }
