@@ -126,7 +126,7 @@ def timed_eager(fn, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def time_decode(w, steps, warmup):
+def time_decode(w, steps, warmup, force_splits=0):
     import torch
 
     import decode_attention_06_amd as fd
@@ -138,8 +138,8 @@ def time_decode(w, steps, warmup):
     sets, lens = decode_inputs(w, copies, dev)
     kv_bytes = 2 * int(lens.sum().item()) * w.kv_heads * w.head_dim * sz   # algorithmic, per step
     dt = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
-    ns = w.n_splits if w.n_splits > 0 else fd.plan_splits(w.batch, w.q_heads, w.kv_heads, w.head_dim,
-                                                          w.max_len, dt, fd.device_cu_count())
+    ns = force_splits or (w.n_splits if w.n_splits > 0 else fd.plan_splits(
+        w.batch, w.q_heads, w.kv_heads, w.head_dim, w.max_len, dt, fd.device_cu_count()))
     rows = w.batch * w.q_heads
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
     o_part = torch.empty((rows, ns, w.head_dim), dtype=torch.float32, device=dev)
@@ -282,6 +282,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
+    ap.add_argument("--n-splits", type=int, default=0, help="force the split count (decode workloads; 0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration)")
@@ -316,7 +317,7 @@ def main():
         info, host = time_bifurcated(w, args.steps, args.warmup)
         dtype = w.dtype
     else:
-        info, host = time_decode(w, args.steps, args.warmup)
+        info, host = time_decode(w, args.steps, args.warmup, args.n_splits)
         dtype = w.dtype
     step_s = info["step_ms"] * 1e-3
     kern_s = info["kernel_ms"] * 1e-3

@@ -181,10 +181,13 @@ int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     const int G = num_q_heads / num_kv_heads;
     const Path path = choose_path(dtype, head_dim, G);
     const int64_t units = int64_t(batch) * num_kv_heads * path.row_blocks;
-    const int64_t target = int64_t(n_cu) * kWgPerCu;
+    // Eight-wave workgroups (few units) fill a CU one at a time.
+    const int64_t wg_per_cu =
+        (path.mfma && fd::mfma_waves_per_unit(int(std::min<int64_t>(units, 1 << 30))) == 8) ? 1 : kWgPerCu;
+    const int64_t target = int64_t(n_cu) * wg_per_cu;
     if (units >= target) return 1;
     int64_t s = (target + units - 1) / units;
-    const int64_t by_len = std::max<int64_t>(1, max_len / (path.mfma ? kMinChunkMfma : kMinChunk));
+    const int64_t by_len = std::max<int64_t>(1, max_len / (path.mfma ? kMinChunkMfma * wg_per_cu : kMinChunk));
     s = std::min<int64_t>(s, by_len);
     s = std::min<int64_t>(s, FD_MAX_SPLITS);
     return int32_t(std::max<int64_t>(s, 1));

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 // with up to 8 * GROUPS pieces costs one memory round trip.  Piece weights are
 // exp(lse_i - max lse); sums run in a fixed order (bitwise repeatable).
 constexpr int CMB_THREADS = 256;
-constexpr int CMB_SLICE = 32;                   // columns per workgroup
+constexpr int CMB_SLICE = 16;                   // columns per workgroup
 constexpr int CMB_BATCH = 8;                    // pieces in flight per thread
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -340,16 +340,33 @@ __global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* _
 #pragma unroll
             for (int e = 0; e < VEC; ++e) ov[u][e] = 0.f;
     }
-    // Row maximum and weight sum over all pieces.
+    // Row maximum and weight sum over all pieces.  With at most
+    // CMB_BATCH * GROUPS pieces the lse values already in registers cover the
+    // row (each piece is held by the DL threads of its group; only dv == 0
+    // counts it in the sum); longer rows read the rest.
+    const bool one_batch = n_parts <= CMB_BATCH * GROUPS;
     float M = -INFINITY;
-    for (int i = tid; i < n_parts; i += CMB_THREADS) M = fmaxf(M, lrow[i]);
+    if (one_batch) {
+#pragma unroll
+        for (int u = 0; u < CMB_BATCH; ++u) M = fmaxf(M, lv[u]);
+    } else {
+        for (int i = tid; i < n_parts; i += CMB_THREADS) M = fmaxf(M, lrow[i]);
+    }
     M = block_max(M, s_red);
     float z = 0.f;
-    if (M != -INFINITY)
-        for (int i = tid; i < n_parts; i += CMB_THREADS) {
-            const float li = lrow[i];
-            z += (li == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2ef);
+    if (M != -INFINITY) {
+        if (one_batch) {
+            if (dv == 0)
+#pragma unroll
+                for (int u = 0; u < CMB_BATCH; ++u)
+                    z += (lv[u] == -INFINITY) ? 0.f : fast_exp2((lv[u] - M) * kLog2ef);
+        } else {
+            for (int i = tid; i < n_parts; i += CMB_THREADS) {
+                const float li = lrow[i];
+                z += (li == -INFINITY) ? 0.f : fast_exp2((li - M) * kLog2ef);
+            }
         }
+    }
     const float Z = block_sum(z, s_red);
 
     float acc[VEC];
@@ -519,7 +536,9 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                               int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
                               float* lse_out, hipStream_t stream) {
-    if (n_parts <= 64) {
+    // One wave per row when rows are plentiful and pieces few; otherwise the
+    // column-slice kernel spreads a row over several workgroups.
+    if (n_parts <= 64 && rows >= 1024) {
         const dim3 grid((unsigned)((rows + CMBW_ROWS - 1) / CMBW_ROWS));
         const dim3 block(64 * CMBW_ROWS);
         const int nv = (head_dim + 63) / 64;

@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 #include "fd_mfma_common.h"
@@ -58,10 +60,11 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
     }
 }
 
-// NRB blocks of 16 query rows per work unit share every K/V load.
-template <int NRB>
-__global__ __launch_bounds__(256, (NRB == 1) ? 2 : 1) void partial_mfma_kernel(const PartialParams p) {
-    constexpr int D = MF_D, NW = MF_NW, ROWS = 16 * NRB;
+// NRB blocks of 16 query rows per work unit share every K/V load; NW waves
+// per workgroup take interleaved 32-token tiles of the unit's piece.
+template <int NRB, int NW>
+__global__ __launch_bounds__(64 * NW, (NRB == 1 && NW == 4) ? 2 : 1) void partial_mfma_kernel(const PartialParams p) {
+    constexpr int D = MF_D, ROWS = 16 * NRB;
     __shared__ float s_acc[NW][ROWS][D];
     __shared__ float s_m[NW][ROWS];
     __shared__ float s_l[NW][ROWS];
@@ -189,15 +192,23 @@ __global__ __launch_bounds__(256, (NRB == 1) ? 2 : 1) void partial_mfma_kernel(c
 
 int mfma_rows_per_block(int G) { return G > 16 ? 32 : 16; }
 
+int mfma_waves_per_unit(int units) { return units <= 8 ? 8 : 4; }
+
 hipError_t launch_partial_mfma(const PartialParams& p, hipStream_t stream) {
     const int G = p.Hq / p.Hkv;
     const int rows = mfma_rows_per_block(G);
     if (p.row_blocks != (G + rows - 1) / rows) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks * p.n_splits));
-    if (rows == 16)
-        hipLaunchKernelGGL(partial_mfma_kernel<1>, grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(partial_mfma_kernel<2>, grid, dim3(256), 0, stream, p);
+    const int64_t units = (int64_t)p.B * p.Hkv * p.row_blocks;
+    const dim3 grid((unsigned)(units * p.n_splits));
+    const bool wide = mfma_waves_per_unit((int)std::min<int64_t>(units, 1 << 30)) == 8;
+    if (rows == 16) {
+        if (wide)
+            hipLaunchKernelGGL((partial_mfma_kernel<1, 8>), grid, dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((partial_mfma_kernel<1, 4>), grid, dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((partial_mfma_kernel<2, 4>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
