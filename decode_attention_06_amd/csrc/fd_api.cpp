@@ -147,10 +147,13 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
         int64_t pc = (int64_t(n_cu) * wg_per_cu + units - 1) / units;
         pc = std::min<int64_t>(pc, std::max<int64_t>(1, Lc / kMinContextPiece));
         b.pc = int32_t(std::max<int64_t>(1, std::min<int64_t>(pc, FD_MAX_SPLITS)));
+        // The decode units run beside the context units in the same launch:
+        // one piece each keeps the partials to combine few.
+        b.pd = 1;
     } else {
         b.pc = fd_plan_splits(S, Hq, Hkv, D, Lc, dtype, n_cu);
+        b.pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
     }
-    b.pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
     return b;
 }
 
@@ -424,8 +427,10 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     p.direct = 0;
     hipError_t e;
     if (plan.mfma_ctx) {
-        // Context part on the matrix cores: every KV head's context rows are
-        // read once per tile of query rows (samples x heads of the group).
+        // One launch: the context part on the matrix cores (every KV head's
+        // context rows read once per tile of query rows = samples x heads of
+        // the group) and, beside it, each sample's decode rows through the
+        // split-KV unit with 16-row blocks.
         fd::BifContextParams c{};
         c.q = q;
         c.k_ctx = k_ctx;
@@ -441,8 +446,17 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
         c.part_stride = P;
         c.part_offset = 0;
         c.scale_log2 = p.scale_log2;
-        e = fd::launch_bif_context(c, s);
-        if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+        p.k = k_dec;
+        p.v = v_dec;
+        p.lens = dec_lens;
+        p.Lmax = Ld;
+        p.kv_stride_h = Ld * D;
+        p.kv_stride_b = int64_t(Hkv) * Ld * D;
+        p.n_splits = pd;
+        p.part_offset = pc;
+        p.row_blocks = (Hq / Hkv + 15) / 16;
+        e = fd::launch_bifurcated(c, p, s);
+        if (e != hipSuccess) return hip_fail(e, "bifurcated kernel launch");
     } else {
         // Context part through the split-KV kernel: every sample reads the
         // same [Hkv, Lc, D] rows (batch stride 0); all Lc rows are valid.
@@ -456,19 +470,18 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
         p.part_offset = 0;
         e = launch_partial(p, path, dtype, D, s);
         if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
+        // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
+        p.k = k_dec;
+        p.v = v_dec;
+        p.lens = dec_lens;
+        p.Lmax = Ld;
+        p.kv_stride_h = Ld * D;
+        p.kv_stride_b = int64_t(Hkv) * Ld * D;
+        p.n_splits = pd;
+        p.part_offset = pc;
+        e = launch_partial(p, path, dtype, D, s);
+        if (e != hipSuccess) return hip_fail(e, "bifurcated decode kernel launch");
     }
-
-    // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
-    p.k = k_dec;
-    p.v = v_dec;
-    p.lens = dec_lens;
-    p.Lmax = Ld;
-    p.kv_stride_h = Ld * D;
-    p.kv_stride_b = int64_t(Hkv) * Ld * D;
-    p.n_splits = pd;
-    p.part_offset = pc;
-    e = launch_partial(p, path, dtype, D, s);
-    if (e != hipSuccess) return hip_fail(e, "bifurcated decode kernel launch");
 
     e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), P, D, out, out_dtype == FD_BF16, lse_out, s);
     if (e != hipSuccess) return hip_fail(e, "bifurcated combine kernel launch");

@@ -28,6 +28,7 @@
 #include "fd_device.h"
 #include "fd_internal.h"
 #include "fd_mfma_common.h"
+#include "fd_mfma_partial.h"
 
 namespace fd {
 namespace {
@@ -127,19 +128,19 @@ __device__ __forceinline__ void wait_vm() {
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+constexpr int CTX_LDS_BYTES = CTX_STAGES * 2 * CTX_TILE_BYTES;   // 64 KiB
+
+// Context role: one work unit (KV head, piece, row tile) given by bid.
 template <int NW>
-__global__ __launch_bounds__(64 * NW, (NW == 4) ? 2 : 1) void bif_context_kernel(const BifContextParams p) {
+__device__ __forceinline__ void context_body(const BifContextParams& p, int bid, char* lds) {
     constexpr int CTX_ROWS = 32 * NW;
     // Loads outstanding per wave for two tiles.
     constexpr int TWO_TILES = 2 * 2 * (8 / NW);
-    // One LDS object per stage (K tile, then V tile), addressed with constant
-    // stage numbers only, so the compiler can tell the tile being read from
-    // the tiles still being written by in-flight loads.
-    __shared__ __attribute__((aligned(16))) char s_t0[2 * CTX_TILE_BYTES], s_t1[2 * CTX_TILE_BYTES],
-        s_t2[2 * CTX_TILE_BYTES], s_t3[2 * CTX_TILE_BYTES];
-    char* const ks[CTX_STAGES] = {s_t0, s_t1, s_t2, s_t3};
-    char* const vs[CTX_STAGES] = {s_t0 + CTX_TILE_BYTES, s_t1 + CTX_TILE_BYTES, s_t2 + CTX_TILE_BYTES,
-                                  s_t3 + CTX_TILE_BYTES};
+    // Stage st holds the K tile at lds + 2 st TILE and the V tile after it;
+    // stages are addressed with constant numbers only.
+    char* const ks[CTX_STAGES] = {lds, lds + 2 * CTX_TILE_BYTES, lds + 4 * CTX_TILE_BYTES, lds + 6 * CTX_TILE_BYTES};
+    char* const vs[CTX_STAGES] = {lds + CTX_TILE_BYTES, lds + 3 * CTX_TILE_BYTES, lds + 5 * CTX_TILE_BYTES,
+                                  lds + 7 * CTX_TILE_BYTES};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -148,7 +149,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4) ? 2 : 1) void bif_context_kernel
 
     // XCD-aware id: ids congruent mod 8 run on one XCD; the row tiles of one
     // unit (KV head, piece) share u_lo and therefore an XCD.
-    const int bid = blockIdx.x;
     const int u_lo = bid % XCDS;
     const int rest = bid / XCDS;
     const int rtile = rest % p.row_tiles;
@@ -262,6 +262,42 @@ __global__ __launch_bounds__(64 * NW, (NW == 4) ? 2 : 1) void bif_context_kernel
     }
 }
 
+// The bifurcated call as one launch with two workgroup roles: context
+// units (above) and the decode part's split-KV units (16-row matrix-core
+// blocks, one piece per unit).  Workgroup ids come in blocks of eight
+// (consecutive ids go to the eight XCDs in turn).  When the decode units are
+// few, blocks alternate between the roles in proportion to their counts, so
+// both kinds run side by side from the start -- the decode part streams its
+// own KV from HBM while the context part keeps the matrix cores busy; when
+// they are many, the context blocks come first.  Either way a context
+// unit's row tiles share one XCD.
+__global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextParams c, const PartialParams d,
+                                                            int n_ctx, int n_dec) {
+    __shared__ __attribute__((aligned(16))) char lds[CTX_LDS_BYTES];
+    static_assert(sizeof(PartialLds<1, 4>) <= CTX_LDS_BYTES, "decode role LDS");
+    const int blk = blockIdx.x / XCDS, lane8 = blockIdx.x % XCDS;
+    const int nb_ctx = (n_ctx + XCDS - 1) / XCDS, nb_dec = (n_dec + XCDS - 1) / XCDS;
+    const int nb = nb_ctx + nb_dec;
+    int ctx_before, ctx_after;
+    if (2 * n_dec <= n_ctx) {
+        // Few decode units: spread them among the context units.
+        ctx_before = (int)((int64_t)blk * nb_ctx / nb);
+        ctx_after = (int)((int64_t)(blk + 1) * nb_ctx / nb);
+    } else {
+        // Many decode units: the long context units start first, so none of
+        // them starts late; the short decode units fill the CUs after them.
+        ctx_before = min(blk, nb_ctx);
+        ctx_after = min(blk + 1, nb_ctx);
+    }
+    if (ctx_after > ctx_before) {
+        const int cid = ctx_before * XCDS + lane8;
+        if (cid < n_ctx) context_body<4>(c, cid, lds);
+    } else {
+        const int did = (blk - ctx_before) * XCDS + lane8;
+        if (did < n_dec) partial_mfma_body<1, 4>(d, did, *reinterpret_cast<PartialLds<1, 4>*>(lds));
+    }
+}
+
 }  // namespace
 
 int bif_context_waves(int, int) { return 4; }
@@ -271,13 +307,13 @@ int bif_context_row_tiles(int S, int G) {
     return (S * G + rows - 1) / rows;
 }
 
-hipError_t launch_bif_context(const BifContextParams& p, hipStream_t stream) {
-    const int units = p.Hkv * p.n_pieces;
-    const int64_t wgs = (int64_t)((units + XCDS - 1) / XCDS) * XCDS * p.row_tiles;
-    if (bif_context_waves(p.S, p.Hq / p.Hkv) == 8)
-        hipLaunchKernelGGL(bif_context_kernel<8>, dim3((unsigned)wgs), dim3(512), 0, stream, p);
-    else
-        hipLaunchKernelGGL(bif_context_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
+hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, hipStream_t stream) {
+    const int units = c.Hkv * c.n_pieces;
+    const int64_t n_ctx = (int64_t)((units + XCDS - 1) / XCDS) * XCDS * c.row_tiles;
+    const int64_t n_dec = (int64_t)d.B * d.Hkv * d.row_blocks * d.n_splits;
+    const int64_t wgs = ((n_ctx + XCDS - 1) / XCDS + (n_dec + XCDS - 1) / XCDS) * XCDS;
+    if (n_ctx >= (1 << 30) || n_dec >= (1 << 30)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bifurcated_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, c, d, (int)n_ctx, (int)n_dec);
     return hipGetLastError();
 }
 

@@ -55,7 +55,11 @@ struct BifContextParams {
 
 int bif_context_waves(int S, int G);        // 8 (one workgroup per CU) or 4
 int bif_context_row_tiles(int S, int G);
-hipError_t launch_bif_context(const BifContextParams& p, hipStream_t stream);
+
+// Whole bifurcated partial stage in one launch: context units (c) and the
+// decode part's split-KV units (d: 16-row matrix-core blocks, i.e.
+// d.row_blocks = ceil(G / 16)) run side by side.
+hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, hipStream_t stream);
 
 // Query rows handled by one work unit of the vector-ALU partial kernel for a
 // GQA group of G query heads: the largest of 8, 4, 2, 1 that divides G.

@@ -1,0 +1,176 @@
+// Split-KV partial work unit on the matrix cores (gfx950, bf16, D = 128),
+// shared by the split-KV kernel and the decode role of the bifurcated
+// kernel.  Internal.  See fd_mfma.hip for the method and the layouts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+#include "fd_internal.h"
+#include "fd_mfma_common.h"
+
+namespace fd {
+namespace {
+
+// Loads one 32-token tile starting at row tb (tb < t1): K in score
+// A-operand layout, V as this lane's 8x8 block (rows 8g .. 8g+7, columns
+// 8i .. 8i+7).  Every load is issued unconditionally; a row index at or
+// beyond t1 is clamped to t1 - 1, a valid row, whose score is masked to -inf
+// later, so no row past the sequence length is ever read.
+__device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t* vbase, int tb, int t1,
+                                          int ktok0, int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
+    const int last = t1 - 1;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int t = min(tb + ktok0 + 4 * blk, last);
+        const uint16_t* src = kbase + (int64_t)t * MF_D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[blk][s] = ld16(src + 32 * s);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = min(tb + 8 * g + j, last);
+        vr[j] = ld16(vbase + (int64_t)t * MF_D + 8 * i);
+    }
+}
+
+// NRB blocks of 16 query rows per work unit share every K/V load; NW waves
+// per workgroup take interleaved 32-token tiles of the unit's piece.
+template <int NRB, int NW>
+struct PartialLds {
+    static constexpr int ROWS = 16 * NRB;
+    float acc[NW][ROWS][MF_D];
+    float m[NW][ROWS];
+    float l[NW][ROWS];
+};
+
+template <int NRB, int NW>
+__device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bid, PartialLds<NRB, NW>& sh) {
+    constexpr int D = MF_D, ROWS = 16 * NRB;
+    auto& s_acc = sh.acc;
+    auto& s_m = sh.m;
+    auto& s_l = sh.l;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
+    const int g = lane >> 4, i = lane & 15;
+
+    int idx = bid;
+    const int split = idx % p.n_splits;
+    idx /= p.n_splits;
+    const int rblk = idx % p.row_blocks;
+    idx /= p.row_blocks;
+    const int kvh = idx % p.Hkv;
+    const int b = idx / p.Hkv;
+    const int G = p.Hq / p.Hkv;
+    const int h0 = kvh * G + rblk * ROWS;
+    const int nr = min(ROWS, G - rblk * ROWS);   // valid query rows in this unit
+
+    int n = p.lens ? p.lens[b] : (int)p.Lmax;
+    n = max(0, min(n, (int)p.Lmax));
+    const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
+    const int t0 = (int)min((int64_t)split * chunk, (int64_t)n);
+    const int t1 = min(t0 + chunk, n);
+
+    // Q^T fragments (B operand of the score product); rows >= nr are zero.
+    bf16x8_t qb[NRB][4];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        const int row = r * 16 + i;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row < nr)
+                v = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h0 + row) * D + 32 * s + 8 * g);
+            qb[r][s] = as_bf16x8(v);
+        }
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h;
+    // Token offsets inside a tile for this lane's K rows (one per token block).
+    const int ktok0 = 8 * (i >> 2) + (i & 3);
+    const float sl2 = p.scale_log2;
+
+    f32x4_t acc[NRB][8], lacc[NRB];
+    float m[NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        m[r] = -INFINITY;
+        lacc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Two register buffers, alternating: the next tile's loads are in
+    // flight while the current tile is computed.  The prefetch is issued
+    // even past the piece's end (its rows clamp to t1 - 1, cache hits), so
+    // every path leaves the same number of loads outstanding and the wait
+    // before each tile covers only that tile's own loads.
+    constexpr int STEP = NW * MF_TILE;
+    u32x4_t ka[2][4], va[8], kb2[2][4], vb2[8];
+    int tb = t0 + wave * MF_TILE;
+    if (tb < t1) {
+        load_tile(kbase, vbase, tb, t1, ktok0, g, i, ka, va);
+        while (true) {
+            load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, kb2, vb2);
+            compute_tile<NRB>(ka, va, qb, tb, t1, g, sl2, m, lacc, acc);
+            tb += STEP;
+            if (tb >= t1) break;
+            load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, ka, va);
+            compute_tile<NRB>(kb2, vb2, qb, tb, t1, g, sl2, m, lacc, acc);
+            tb += STEP;
+            if (tb >= t1) break;
+        }
+    }
+
+    // Hand the wave state (row sums already complete in lacc) to LDS.
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        const int row = r * 16 + i;
+        if (row < nr) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) s_acc[wave][row][8 * (4 * g + ii) + e] = acc[r][e][ii];
+            if (g == 0) {
+                s_m[wave][row] = m[r];
+                s_l[wave][row] = lacc[r][0];
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int x = tid; x < nr * D; x += NW * 64) {
+        const int row = x / D, d = x % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][row]);
+        float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float a = fast_exp2(s_m[w][row] - M);
+                L = fmaf(s_l[w][row], a, L);
+                A = fmaf(s_acc[w][row][d], a, A);
+            }
+        }
+        const float o = (L > 0.f) ? A / L : 0.f;
+        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
+        const int64_t orow = (int64_t)b * p.Hq + h0 + row;
+        if (p.direct) {
+            store_out(p.out, orow * D + d, o, p.out_bf16);
+            if (d == 0 && p.lse_out) p.lse_out[orow] = lse;
+        } else {
+            const int64_t slot = orow * p.part_stride + p.part_offset + split;
+            p.o_part[slot * D + d] = o;
+            if (d == 0) p.lse_part[slot] = lse;
+        }
+    }
+}
+
+}  // namespace
+}  // namespace fd
