@@ -189,7 +189,39 @@ def time_decode(w, steps, warmup, force_splits=0):
     return info, (host, lens.cpu().numpy())
 
 
-def time_bifurcated(w, steps, warmup):
+def time_concatenated(w, sets, dl, steps):
+    """Split-KV decode attention over [context ; own decode rows] per sample
+    (the non-bifurcated way to get the same result): µs per step."""
+    import torch
+
+    import decode_attention_06_amd as fd
+
+    t = sets[0]
+    S, Hkv, Lc, Ld, D = w.samples, w.kv_heads, w.ctx_len, w.dec_max, w.head_dim
+    kc = torch.empty((S, Hkv, Lc + Ld, D), dtype=t["k_ctx"].dtype, device=t["k_ctx"].device)
+    vc = torch.empty_like(kc)
+    kc[:, :, :Lc] = t["k_ctx"].unsqueeze(0)
+    vc[:, :, :Lc] = t["v_ctx"].unsqueeze(0)
+    kc[:, :, Lc:] = t["k_dec"]
+    vc[:, :, Lc:] = t["v_dec"]
+    lens = (dl + Lc).to(torch.int32)
+    out = torch.empty((S, w.q_heads, D), dtype=t["q"].dtype, device=kc.device)
+    ns = fd.plan_splits(S, w.q_heads, Hkv, D, Lc + Ld, fd.FD_BF16, fd.device_cu_count())
+    ws = torch.empty(max(1, fd.decode_workspace_size(S, w.q_heads, Hkv, D, Lc + Ld, fd.FD_BF16, ns)),
+                     dtype=torch.uint8, device=kc.device)
+
+    def step(j):
+        fd.decode_attn(t["q"], kc, vc, lens, n_splits=ns, out=out, workspace=ws)
+
+    for j in range(3):
+        step(j)
+    ms = timed_graph(step, steps)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return ms, ns
+
+
+def time_bifurcated(w, steps, warmup, compare_concat=False):
     import torch
 
     import decode_attention_06_amd as fd
@@ -218,6 +250,8 @@ def time_bifurcated(w, steps, warmup):
     step_ms = timed_graph(step, steps)
     info = {"n_splits": None, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": step_ms,
             "eager_step_ms": eager_ms, "probe_gbs": None, "kernel": "bifurcated (whole call)", "flops": flops}
+    if compare_concat:
+        info["concat_ms"], info["concat_splits"] = time_concatenated(w, sets, dl, max(5, steps // 4))
     return info, None
 
 
@@ -283,6 +317,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--n-splits", type=int, default=0, help="force the split count (decode workloads; 0 = planner)")
+    ap.add_argument("--compare-concat", action="store_true",
+                    help="bifurcated workloads: also time split-KV decode over the concatenated cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration)")
@@ -314,7 +350,7 @@ def main():
     w = WORKLOADS[args.workload]
     bif = w.name in {b.name for b in configs.ALL_BIFURCATED}
     if bif:
-        info, host = time_bifurcated(w, args.steps, args.warmup)
+        info, host = time_bifurcated(w, args.steps, args.warmup, args.compare_concat)
         dtype = w.dtype
     else:
         info, host = time_decode(w, args.steps, args.warmup, args.n_splits)
@@ -372,6 +408,11 @@ def main():
     if bif:
         line["roofline"]["mfma_tflops"] = round(info["flops"] / step_s / 1e12, 2)
         line["roofline"]["mfma_frac"] = round(info["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        if "concat_ms" in info:
+            line["concatenated_us_per_step"] = round(info["concat_ms"] * 1e3, 3)
+            line["speedup_vs_concatenated"] = round(info["concat_ms"] / info["step_ms"], 3)
+            log(f"[bench] same result by split-KV over the concatenated cache: {info['concat_ms'] * 1e3:.2f} us "
+                f"({info['concat_splits']} pieces); bifurcated speedup {info['concat_ms'] / info['step_ms']:.2f}x")
     print(json.dumps(line), flush=True)
     return 0
 
