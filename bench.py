@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATION_BYTES = 1 << 30
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_BIFURCATED)}
+WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_PAGED + configs.ALL_BIFURCATED)}
 DEFAULT_WORKLOAD = configs.CODELLAMA34B_SHARE.name
 
 
@@ -62,6 +62,28 @@ def decode_inputs(w, copies, dev):
         v = synth.device_normal((w.batch, w.kv_heads, w.max_len, w.head_dim), s + 2, w.dtype, dev)
         sets.append((q, k, v))
     return sets, lens
+
+
+def paged_inputs(w, copies, dev):
+    """Page pools (one per copy) sharing one shuffled block table."""
+    import torch
+
+    P = w.page_size
+    per_seq = -(-w.max_len // P)
+    n_pages = 1 + w.batch * per_seq
+    table = torch.from_numpy(synth.shuffled_block_table(w.batch, per_seq, w.seed + 11)).to(dev)
+    if w.ragged:
+        lens = synth.device_lengths(w.batch, w.max_len // 2, w.max_len, w.seed + 7, dev)
+    else:
+        lens = torch.full((w.batch,), w.max_len, dtype=torch.int32, device=dev)
+    sets = []
+    for c in range(copies):
+        s = w.seed + 1000 * c
+        q = synth.device_normal((w.batch, w.q_heads, w.head_dim), s, w.dtype, dev)
+        kp = synth.device_normal((n_pages, w.kv_heads, P, w.head_dim), s + 1, w.dtype, dev)
+        vp = synth.device_normal((n_pages, w.kv_heads, P, w.head_dim), s + 2, w.dtype, dev)
+        sets.append((q, kp, vp))
+    return sets, table, lens
 
 
 def bifurcated_inputs(w, copies, dev):
@@ -187,6 +209,55 @@ def time_decode(w, steps, warmup, force_splits=0):
     }
     host = [t.detach().float().cpu().numpy() for t in sets[0]]
     return info, (host, lens.cpu().numpy())
+
+
+def time_paged(w, steps, warmup, force_splits=0):
+    """Decode over a paged cache.  The dominant kernel's time is the step's
+    minus the combine's, the combine timed alone on the same partials (the
+    paged entry point runs both launches)."""
+    import torch
+
+    import decode_attention_06_amd as fd
+
+    dev = torch.device("cuda:0")
+    sz = 2 if w.dtype == "bf16" else 4
+    alloc_bytes = 2 * w.batch * w.kv_heads * w.max_len * w.head_dim * sz
+    copies = max(2, math.ceil(ROTATION_BYTES / alloc_bytes))
+    sets, table, lens = paged_inputs(w, copies, dev)
+    kv_bytes = 2 * int(lens.sum().item()) * w.kv_heads * w.head_dim * sz
+    dt = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
+    max_len = table.shape[1] * w.page_size
+    ns = force_splits or (w.n_splits if w.n_splits > 0 else fd.plan_splits(
+        w.batch, w.q_heads, w.kv_heads, w.head_dim, max_len, dt, fd.device_cu_count()))
+    rows = w.batch * w.q_heads
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
+    ws = torch.empty(max(1, fd.decode_workspace_size(w.batch, w.q_heads, w.kv_heads, w.head_dim, max_len, dt, ns)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(j):
+        q, kp, vp = sets[j % copies]
+        fd.decode_attn_paged(q, kp, vp, table, lens, n_splits=ns, out=out, workspace=ws)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    eager_ms = timed_eager(step, steps)
+    step_ms = timed_graph(step, steps)
+    combine_ms = 0.0
+    if ns > 1:
+        lse_bytes = (rows * ns * 4 + 255) // 256 * 256
+        lse_part = ws[:rows * ns * 4].view(torch.float32).view(rows, ns)
+        o_part = ws[lse_bytes:lse_bytes + rows * ns * w.head_dim * 4].view(torch.float32).view(rows, ns, w.head_dim)
+        combine_ms = timed_graph(lambda j: fd.lse_combine(o_part, lse_part, out=out.view(rows, w.head_dim)), steps)
+    info = {
+        "n_splits": ns, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms,
+        "kernel_ms": step_ms - combine_ms, "eager_step_ms": eager_ms, "probe_gbs": None,
+        "kernel": "partial_mfma_kernel" if (w.dtype == "bf16" and w.head_dim == 128 and
+                                             w.q_heads // w.kv_heads >= 4) else "partial_valu_kernel",
+        "kernel_timing": "step minus the combine timed alone",
+        "flops": 4 * int(lens.sum().item()) * w.q_heads * w.head_dim,
+    }
+    return info, None
 
 
 def time_concatenated(w, sets, dl, steps):
@@ -352,6 +423,9 @@ def main():
     if bif:
         info, host = time_bifurcated(w, args.steps, args.warmup, args.compare_concat)
         dtype = w.dtype
+    elif getattr(w, "page_size", 0) > 0:
+        info, host = time_paged(w, args.steps, args.warmup, args.n_splits)
+        dtype = w.dtype
     else:
         info, host = time_decode(w, args.steps, args.warmup, args.n_splits)
         dtype = w.dtype
@@ -376,6 +450,8 @@ def main():
     else:
         config.update(batch=w.batch, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
                       kv_len=w.max_len, lens="uniform [L/2, L]" if w.ragged else "all L")
+        if w.page_size:
+            config.update(page_size=w.page_size, pages="shuffled pool, one block table")
     line = {
         "metric": METRIC,
         "value": round(value_tbs, 4),
@@ -405,6 +481,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if "kernel_timing" in info:
+        line["roofline"]["kernel_timing"] = info["kernel_timing"]
     if bif:
         line["roofline"]["mfma_tflops"] = round(info["flops"] / step_s / 1e12, 2)
         line["roofline"]["mfma_frac"] = round(info["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)

@@ -28,6 +28,9 @@ SIGNATURES = {
                                                ctypes.POINTER(_c_sz)]),
     "fd_decode_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                 _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_decode_attn_paged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32,
+                                      _c_vp, _c_sz, _c_vp]),
     "fd_bifurcated_attn_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
                                                    ctypes.POINTER(_c_sz)]),
     "fd_bifurcated_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -160,6 +163,46 @@ def decode_attn(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=
                               B, Hq, Hkv, D, Lmax, dt, int(n_splits), _dev_ptr(out, "out"), _dtype_code(out),
                               _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def decode_attn_paged(q, k_pages, v_pages, block_table, lens=None, n_splits=0, out=None, out_dtype=None,
+                      scale=0.0, return_lse=False, workspace=None, stream=None):
+    """Split-KV decode attention over a paged KV cache (fd_decode_attn_paged).
+
+    q [B, Hq, D]; k_pages, v_pages [num_pages, Hkv, page_size, D];
+    block_table int32 [B, max_pages_per_seq] of page ids on the device; lens
+    int32 [B] on the device or None (= max_pages_per_seq * page_size).
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape or block_table.dim() != 2:
+        raise FdError(FD_ERR_INVALID_ARG,
+                      "expected q [B,Hq,D], k_pages, v_pages [pages,Hkv,page_size,D], block_table [B,max_pages]")
+    B, Hq, D = q.shape
+    n_pages, Hkv, page_size, Dk = k_pages.shape
+    max_pages = block_table.shape[1]
+    if Dk != D or block_table.shape[0] != B or block_table.dtype != torch.int32:
+        raise FdError(FD_ERR_INVALID_ARG, "paged shapes do not match q, or block_table is not int32 [B, *]")
+    dt = _dtype_code(q)
+    if _dtype_code(k_pages) != dt or _dtype_code(v_pages) != dt:
+        raise FdError(FD_ERR_UNSUPPORTED, "q, k and v must share one dtype")
+    if lens is not None and (lens.dtype != torch.int32 or lens.shape != (B,)):
+        raise FdError(FD_ERR_INVALID_ARG, "lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise FdError(FD_ERR_INVALID_ARG, "out must be [B, Hq, D]")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = decode_workspace_size(B, Hq, Hkv, D, max_pages * page_size, dt, n_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fd_decode_attn_paged(_dev_ptr(q, "q"), _dev_ptr(k_pages, "k_pages"), _dev_ptr(v_pages, "v_pages"),
+                                    _dev_ptr(block_table, "block_table"), _opt_ptr(lens, "lens"), B, Hq, Hkv, D,
+                                    page_size, n_pages, max_pages, dt, int(n_splits), _dev_ptr(out, "out"),
+                                    _dtype_code(out), _opt_ptr(lse, "lse"), float(scale),
+                                    _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
     return (out, lse) if return_lse else out
 
 

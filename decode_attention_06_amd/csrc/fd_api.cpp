@@ -7,6 +7,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -246,15 +247,15 @@ fd_status fd_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
     return FD_OK;
 }
 
-fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int32_t* lens, int32_t B,
-                         int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype,
-                         int32_t n_splits, void* out, int32_t out_dtype, float* lse_out, float scale,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+// Shared tail of fd_decode_attn and fd_decode_attn_paged: `p` carries the
+// cache addressing (dense strides or the page table); this fills in the
+// rest, launches the partial kernel and, for several pieces, the combine.
+static fd_status run_decode(fd::PartialParams p, const void* q, const int32_t* lens, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype, int32_t n_splits,
+                            void* out, int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     FD_TRY(check_out_dtype(out_dtype));
     FD_TRY(check_ptr(q, 16, "q"));
-    FD_TRY(check_ptr(k, 16, "k"));
-    FD_TRY(check_ptr(v, 16, "v"));
     FD_TRY(check_ptr(out, 16, "out"));
     if (lens && !aligned(lens, 4)) return fail(FD_ERR_INVALID_ARG, "lens is not 4-byte aligned");
     if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
@@ -272,16 +273,11 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
     }
 
     const Path path = choose_path(dtype, D, Hq / Hkv);
-    fd::PartialParams p{};
     p.q = q;
-    p.k = k;
-    p.v = v;
     p.lens = lens;
     p.out = out;
     p.lse_out = lse_out;
     p.Lmax = Lmax;
-    p.kv_stride_h = Lmax * D;
-    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -308,6 +304,53 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
         if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
     }
     return FD_OK;
+}
+
+fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int32_t* lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype,
+                         int32_t n_splits, void* out, int32_t out_dtype, float* lse_out, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    fd::PartialParams p{};
+    p.k = k;
+    p.v = v;
+    p.kv_stride_h = Lmax * D;
+    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
+    return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
+                      workspace, workspace_bytes, stream);
+}
+
+fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* lens, int32_t B, int32_t Hq,
+                               int32_t Hkv, int32_t D, int32_t page_size, int64_t num_pages,
+                               int32_t max_pages, int32_t dtype, int32_t n_splits, void* out,
+                               int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [16, 2^20]", page_size);
+    if (num_pages <= 0 || num_pages > INT32_MAX)
+        return fail(FD_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31 - 1]", (long long)num_pages);
+    if (max_pages <= 0) return fail(FD_ERR_INVALID_ARG, "max_pages_per_seq must be positive (got %d)", max_pages);
+    const int64_t Lmax = int64_t(max_pages) * page_size;
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    FD_TRY(check_ptr(k_pages, 16, "k_pages"));
+    FD_TRY(check_ptr(v_pages, 16, "v_pages"));
+    FD_TRY(check_ptr(block_table, 4, "block_table"));
+    fd::PartialParams p{};
+    p.k = k_pages;
+    p.v = v_pages;
+    p.block_table = block_table;
+    p.bt_stride = max_pages;
+    p.kv_stride_h = int64_t(page_size) * D;
+    p.page_stride = int64_t(Hkv) * page_size * D;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    p.page_shift = shift;
+    p.n_pages = int32_t(num_pages);
+    return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
+                      workspace, workspace_bytes, stream);
 }
 
 fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, const int32_t* lens,

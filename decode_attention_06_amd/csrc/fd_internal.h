@@ -16,8 +16,8 @@ namespace fd {
 // row (the online softmax).
 struct PartialParams {
     const void* q;          // [B, Hq, D]
-    const void* k;          // element (b, kvh, t, d) at b*kv_stride_b + kvh*kv_stride_h + t*D + d
-    const void* v;
+    const void* k;          // dense: element (b, kvh, t, d) at b*kv_stride_b + kvh*kv_stride_h + t*D + d
+    const void* v;          // paged: see block_table
     const int32_t* lens;    // [B] valid rows per sequence, or nullptr = Lmax
     void* out;              // direct mode: final output [B, Hq, D]
     float* lse_out;         // direct mode: [B, Hq] natural-log lse, or nullptr
@@ -34,6 +34,15 @@ struct PartialParams {
     float scale_log2;       // softmax scale * log2(e)
     int32_t out_bf16;       // direct mode output dtype
     int32_t direct;         // 1: n_splits == 1, write the final output
+    // Paged cache (block_table != nullptr): row t of (b, kvh) is row
+    // t & (page_size - 1) of page block_table[b * bt_stride + (t >> page_shift)],
+    // at element page * page_stride + kvh * kv_stride_h + (t & (page_size - 1)) * D.
+    // Page ids outside [0, n_pages) are clamped into it.
+    const int32_t* block_table;
+    int64_t bt_stride;      // table entries per sequence
+    int64_t page_stride;    // elements per page (Hkv * page_size * D)
+    int32_t page_shift;     // log2(page_size), page_size >= 16
+    int32_t n_pages;
 };
 
 // Context part of a bifurcated call on the matrix cores (bf16, head_dim

@@ -25,6 +25,7 @@
 
 #include "fd_device.h"
 #include "fd_internal.h"
+#include "fd_kv_rows.h"
 
 namespace fd {
 namespace {
@@ -78,7 +79,7 @@ __device__ __forceinline__ void merge_weights(float m, float m2, float& mn, floa
     w2 = fast_exp2(m2 - ref);
 }
 
-template <typename T, int D, int GB>
+template <typename T, int D, int GB, bool PAGED>
 __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p) {
     constexpr int EPL = Vec16<T>::N;     // elements per lane per row
     constexpr int LPR = D / EPL;         // lanes per KV row
@@ -126,8 +127,14 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
     }
 
-    const T* kb = static_cast<const T*>(p.k) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + c * EPL;
-    const T* vb = static_cast<const T*>(p.v) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + c * EPL;
+    // Dense: the (b, kvh) slice's first row.  Paged: the pool; rows are
+    // found per 16-row group (a wave's tile covers NG groups; the row of
+    // load u lies in group u * RPW / 16).
+    const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
+    const T* kb = static_cast<const T*>(p.k) + slice + c * EPL;
+    const T* vb = static_cast<const T*>(p.v) + slice + c * EPL;
+    constexpr int NG = WAVE_TOK >= 16 ? WAVE_TOK / 16 : 1;
+    static_assert(16 % RPW == 0, "a load's rows must stay inside one 16-row group");
 
     float m[GB], l[GB], acc[GB][EPL];
 #pragma unroll
@@ -143,11 +150,30 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         // Unconditional loads; rows at or beyond t1 clamp to t1 - 1 (a valid
         // row whose score is masked below), so the loads issue back to back.
         uint4 kr[U], vr[U];
+        if constexpr (PAGED) {
+            const int last = t1 - 1;
+            int gs[NG];
+            int64_t go[NG];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = min(tb + u * RPW + r, t1 - 1);
-            kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
-            vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
+            for (int h = 0; h < NG; ++h) {
+                gs[h] = kv_group_start(tb + 16 * h, last);
+                go[h] = kv_row_offset<true, D>(p, b, kvh, gs[h]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int h = (NG > 1) ? (u * RPW) / 16 : 0;
+                const int t = min(tb + u * RPW + r, last);
+                const int64_t off = go[h] + (int64_t)(t - gs[h]) * D;
+                kr[u] = *reinterpret_cast<const uint4*>(kb + off);
+                vr[u] = *reinterpret_cast<const uint4*>(vb + off);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int t = min(tb + u * RPW + r, t1 - 1);
+                kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
+                vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
+            }
         }
 
         // Scores (log2 domain).  All lanes take part in the DPP sums.
@@ -497,18 +523,24 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 hipError_t launch_valu_rows(const PartialParams& p, int rows_per_block, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks * p.n_splits));
     const dim3 block(256);
     switch (rows_per_block) {
-        case 1: hipLaunchKernelGGL((partial_valu_kernel<T, D, 1>), grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((partial_valu_kernel<T, D, 2>), grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((partial_valu_kernel<T, D, 4>), grid, block, 0, stream, p); break;
-        case 8: hipLaunchKernelGGL((partial_valu_kernel<T, D, 8>), grid, block, 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((partial_valu_kernel<T, D, 1, PAGED>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((partial_valu_kernel<T, D, 2, PAGED>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((partial_valu_kernel<T, D, 4, PAGED>), grid, block, 0, stream, p); break;
+        case 8: hipLaunchKernelGGL((partial_valu_kernel<T, D, 8, PAGED>), grid, block, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_valu_layout(const PartialParams& p, int rows_per_block, hipStream_t stream) {
+    return p.block_table ? launch_valu_rows<T, D, true>(p, rows_per_block, stream)
+                         : launch_valu_rows<T, D, false>(p, rows_per_block, stream);
 }
 
 }  // namespace
@@ -516,11 +548,11 @@ hipError_t launch_valu_rows(const PartialParams& p, int rows_per_block, hipStrea
 hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, int rows_per_block,
                                hipStream_t stream) {
     if (dtype == 0) {
-        if (head_dim == 64) return launch_valu_rows<float, 64>(p, rows_per_block, stream);
-        if (head_dim == 128) return launch_valu_rows<float, 128>(p, rows_per_block, stream);
+        if (head_dim == 64) return launch_valu_layout<float, 64>(p, rows_per_block, stream);
+        if (head_dim == 128) return launch_valu_layout<float, 128>(p, rows_per_block, stream);
     } else {
-        if (head_dim == 64) return launch_valu_rows<uint16_t, 64>(p, rows_per_block, stream);
-        if (head_dim == 128) return launch_valu_rows<uint16_t, 128>(p, rows_per_block, stream);
+        if (head_dim == 64) return launch_valu_layout<uint16_t, 64>(p, rows_per_block, stream);
+        if (head_dim == 128) return launch_valu_layout<uint16_t, 128>(p, rows_per_block, stream);
     }
     return hipErrorInvalidValue;
 }

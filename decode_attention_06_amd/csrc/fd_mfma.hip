@@ -39,10 +39,23 @@
 namespace fd {
 namespace {
 
-template <int NRB, int NW>
+template <int NRB, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, (NRB == 1 && NW == 4) ? 2 : 1) void partial_mfma_kernel(const PartialParams p) {
     __shared__ PartialLds<NRB, NW> sh;
-    partial_mfma_body<NRB, NW>(p, blockIdx.x, sh);
+    partial_mfma_body<NRB, NW, PAGED>(p, blockIdx.x, sh);
+}
+
+template <bool PAGED>
+hipError_t launch_mfma_layout(const PartialParams& p, dim3 grid, int rows, bool wide, hipStream_t stream) {
+    if (rows == 16) {
+        if (wide)
+            hipLaunchKernelGGL((partial_mfma_kernel<1, 8, PAGED>), grid, dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED>), grid, dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((partial_mfma_kernel<2, 4, PAGED>), grid, dim3(256), 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -58,15 +71,8 @@ hipError_t launch_partial_mfma(const PartialParams& p, hipStream_t stream) {
     const int64_t units = (int64_t)p.B * p.Hkv * p.row_blocks;
     const dim3 grid((unsigned)(units * p.n_splits));
     const bool wide = mfma_waves_per_unit((int)std::min<int64_t>(units, 1 << 30)) == 8;
-    if (rows == 16) {
-        if (wide)
-            hipLaunchKernelGGL((partial_mfma_kernel<1, 8>), grid, dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((partial_mfma_kernel<1, 4>), grid, dim3(256), 0, stream, p);
-    } else {
-        hipLaunchKernelGGL((partial_mfma_kernel<2, 4>), grid, dim3(256), 0, stream, p);
-    }
-    return hipGetLastError();
+    return p.block_table ? launch_mfma_layout<true>(p, grid, rows, wide, stream)
+                         : launch_mfma_layout<false>(p, grid, rows, wide, stream);
 }
 
 }  // namespace fd

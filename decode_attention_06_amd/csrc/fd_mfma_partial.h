@@ -9,6 +9,7 @@
 
 #include "fd_device.h"
 #include "fd_internal.h"
+#include "fd_kv_rows.h"
 #include "fd_mfma_common.h"
 
 namespace fd {
@@ -36,6 +37,36 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
     }
 }
 
+// Paged form of load_tile: the tile (16-row aligned) covers two 16-row
+// groups, each inside one page.  A lane's K rows lie in group i / 8 and its
+// V rows in group g / 2; rows at or beyond t1 clamp to t1 - 1 as above, and
+// kv_group_start gives the group that then holds them.
+__device__ __forceinline__ void load_tile_paged(const PartialParams& p, int b, int kvh, int tb, int t1,
+                                                int ktok0, int g, int i, u32x4_t (&kr)[2][4],
+                                                u32x4_t (&vr)[8]) {
+    const int last = t1 - 1;
+    const int s0 = kv_group_start(tb, last), s1 = kv_group_start(tb + 16, last);
+    const int64_t o0 = kv_row_offset<true, MF_D>(p, b, kvh, s0);
+    const int64_t o1 = kv_row_offset<true, MF_D>(p, b, kvh, s1);
+    const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
+    const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
+    const bool khi = i >= 8, vhi = g >= 2;
+    const uint16_t* kg = kpool + (khi ? o1 : o0) - (int64_t)(khi ? s1 : s0) * MF_D + 8 * g;
+    const uint16_t* vg = vpool + (vhi ? o1 : o0) - (int64_t)(vhi ? s1 : s0) * MF_D + 8 * i;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int t = min(tb + ktok0 + 4 * blk, last);
+        const uint16_t* src = kg + (int64_t)t * MF_D;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[blk][s] = ld16(src + 32 * s);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = min(tb + 8 * g + j, last);
+        vr[j] = ld16(vg + (int64_t)t * MF_D);
+    }
+}
+
 // NRB blocks of 16 query rows per work unit share every K/V load; NW waves
 // per workgroup take interleaved 32-token tiles of the unit's piece.
 template <int NRB, int NW>
@@ -46,7 +77,7 @@ struct PartialLds {
     float l[NW][ROWS];
 };
 
-template <int NRB, int NW>
+template <int NRB, int NW, bool PAGED = false>
 __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bid, PartialLds<NRB, NW>& sh) {
     constexpr int D = MF_D, ROWS = 16 * NRB;
     auto& s_acc = sh.acc;
@@ -89,8 +120,9 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         }
     }
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h;
-    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h;
+    const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + slice;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + slice;
     // Token offsets inside a tile for this lane's K rows (one per token block).
     const int ktok0 = 8 * (i >> 2) + (i & 3);
     const float sl2 = p.scale_log2;
@@ -112,15 +144,21 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // before each tile covers only that tile's own loads.
     constexpr int STEP = NW * MF_TILE;
     u32x4_t ka[2][4], va[8], kb2[2][4], vb2[8];
+    auto load = [&](int at, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
+        if constexpr (PAGED)
+            load_tile_paged(p, b, kvh, at, t1, ktok0, g, i, kr, vr);
+        else
+            load_tile(kbase, vbase, at, t1, ktok0, g, i, kr, vr);
+    };
     int tb = t0 + wave * MF_TILE;
     if (tb < t1) {
-        load_tile(kbase, vbase, tb, t1, ktok0, g, i, ka, va);
+        load(tb, ka, va);
         while (true) {
-            load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, kb2, vb2);
+            load(tb + STEP, kb2, vb2);
             compute_tile<NRB>(ka, va, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;
-            load_tile(kbase, vbase, tb + STEP, t1, ktok0, g, i, ka, va);
+            load(tb + STEP, ka, va);
             compute_tile<NRB>(kb2, vb2, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;

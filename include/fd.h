@@ -21,6 +21,10 @@
  *       sections "Tiivistelmä" and "Tilastot": attention over a shared
  *       context KV plus per-sample decode KV, exact, with the context KV
  *       read once; GQA/MQA heads share KV heads.
+ *  [MW] gyaansetu.com article on the memory wall of LLM decoding (Kannada),
+ *       section "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", paragraph on
+ *       PagedAttention: KV cache entries kept in fixed-size blocks that are
+ *       allocated non-contiguously and found through an indirection table.
  *
  * Conventions shared by every entry point
  *  - Every data pointer is a device pointer owned by the caller.  The
@@ -146,6 +150,36 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
                          int32_t head_dim, int64_t max_len, int32_t dtype,
                          int32_t n_splits, void* out, int32_t out_dtype, float* lse_out,
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fd_decode_attn_paged - fd_decode_attn over a paged KV cache ([MW] "ಮೆಮೊರಿ
+ * ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", PagedAttention: fixed-size blocks found
+ * through an indirection table).  The result is the result of
+ * fd_decode_attn on the gathered cache, bit for bit, for the same n_splits.
+ *
+ *   k_pages, v_pages  [num_pages, Hkv, page_size, D]: page p holds, for each
+ *                     KV head, page_size consecutive rows
+ *   block_table       device int32 [B, max_pages_per_seq]: row t of sequence
+ *                     b is row t % page_size of page
+ *                     block_table[b][t / page_size]; only entries that cover
+ *                     rows < lens[b] are read.  Entries must lie in
+ *                     [0, num_pages); an entry outside is clamped into it (a
+ *                     wrong result, never a read outside the pool)
+ *   page_size         power of two, 16 <= page_size <= 2^20
+ *   num_pages         pages in the pool, 1 .. 2^31 - 1
+ *   max_pages_per_seq table columns; rows per sequence are at most
+ *                     max_len = max_pages_per_seq * page_size (<= 2^30)
+ *   lens              device int32 [B], each in [1, max_len]; NULL = max_len
+ *   everything else   as in fd_decode_attn; the workspace size is
+ *                     fd_decode_attn_workspace_size(..., max_len, ...)
+ */
+fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* lens, int32_t batch,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int64_t num_pages, int32_t max_pages_per_seq,
+                               int32_t dtype, int32_t n_splits, void* out, int32_t out_dtype,
+                               float* lse_out, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * fd_decode_attn_partials - the partial stage of fd_decode_attn on its own

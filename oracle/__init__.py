@@ -9,5 +9,6 @@ from .fp64 import (  # noqa: F401
     bifurcated_attention,
     default_scale,
     lse_combine,
+    paged_attention,
     split_partials,
 )

@@ -17,6 +17,10 @@ Sources (the pages this follows; cited by title and section):
   sposta grandi tensori intermedi attraverso la HBM" (attention = scores from
   query and keys, normalised, then combined with the values) and "La softmax
   online evita di memorizzare l'intera matrice dei punteggi".
+* [MW]  gyaansetu.com article on the memory wall of LLM decoding (Kannada),
+  section "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", paragraph on
+  PagedAttention: KV cache entries are kept in fixed-size blocks, allocated
+  non-contiguously and found through an indirection table.
 * [BA]  "Effiziente Verarbeitung und Analyse von Inhalten durch bifurkierte
   Aufmerksamkeit für Single-Context-Batch-Sampling" (linnk.ai), section
   "Tiivistelmä": incremental-decode attention is split into a part over the
@@ -49,6 +53,7 @@ __all__ = [
     "bifurcated_attention",
     "split_partials",
     "lse_combine",
+    "paged_attention",
 ]
 
 
@@ -119,6 +124,56 @@ def attention(q, k, v, lens=None, scale=None):
         for g in range(Hkv):
             rows = slice(g * G, (g + 1) * G)
             o, l = _attend_rows(q[b, rows], k[b, g, :n], v[b, g, :n], scale)
+            out[b, rows] = o
+            lse[b, rows] = l
+    return out, lse
+
+
+def paged_attention(q, k_pages, v_pages, block_table, lens=None, scale=None):
+    """Exact decode attention over a paged KV cache.
+
+    q                 [B, Hq, D]
+    k_pages, v_pages  [n_pages, Hkv, P, D]  pages of P rows for each KV head
+    block_table       [B, max_pages] integer page ids
+    lens              [B] integers in [1, max_pages * P] (None: all of them)
+    Returns out [B, Hq, D] and lse [B, Hq], as ``attention``.
+
+    [MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", PagedAttention: the cache
+    rows sit in fixed-size blocks reached through an indirection table; the
+    attention itself does not change.  Logical row t of sequence b is row
+    t mod P of page block_table[b, t div P].  Those rows, in order, are the
+    sequence's cache; only the table entries that cover rows below lens[b]
+    are read, and each of them must name a page of the pool.
+    """
+    q, k_pages, v_pages = _as_f64(q), _as_f64(k_pages), _as_f64(v_pages)
+    B, Hq, D = q.shape
+    n_pages, Hkv, P, Dk = k_pages.shape
+    table = np.asarray(block_table, dtype=np.int64)
+    if Dk != D or v_pages.shape != k_pages.shape or table.ndim != 2 or table.shape[0] != B:
+        raise ValueError("shape mismatch between q, the pages and the block table")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    Lmax = table.shape[1] * P
+    if lens is None:
+        lens = np.full(B, Lmax, dtype=np.int64)
+    lens = np.asarray(lens, dtype=np.int64)
+    if scale is None:
+        scale = default_scale(D)
+    out = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        n = int(lens[b])
+        if not 1 <= n <= Lmax:
+            raise ValueError(f"lens[{b}]={n} outside [1, {Lmax}]")
+        t = np.arange(n)
+        page = table[b, t // P]
+        slot = t % P
+        if page.min() < 0 or page.max() >= n_pages:
+            raise ValueError(f"sequence {b} names a page outside [0, {n_pages})")
+        for g in range(Hkv):
+            rows = slice(g * G, (g + 1) * G)
+            o, l = _attend_rows(q[b, rows], k_pages[page, g, slot], v_pages[page, g, slot], scale)
             out[b, rows] = o
             lse[b, rows] = l
     return out, lse

@@ -55,6 +55,16 @@ EXAMPLES = {
          "o_part": [[[2.0]], [[6.0]], [[0.0]]], "lse_part": [[0.0], [LN3], [None]],
          "out": [[5.0]], "lse": [LN4]},
     ],
+    "paged_examples": [
+        {"name": "reversed_pages_exclude_the_tail",
+         "cite": "memory-wall page (gyaansetu.com), section on fighting the memory wall, PagedAttention paragraph: cache rows in fixed-size blocks reached through an indirection table",
+         "derivation": "page size 2. Sequence 0 uses pages [1, 0] and 3 rows: page1 row0 (K 0, V 6), page1 row1 (K ln 2, V 0), page0 row0 (K ln 3, V 2); page0 row1 (K 100) lies past the length. Weights 1:2:3 -> out = (6 + 0 + 3*2)/6 = 2, lse = ln 6. Sequence 1 uses page 2 and 1 row (K 5, V 50) -> out 50, lse 5",
+         "scale": 1.0, "q": [[[1.0]], [[1.0]]], "page_size": 2,
+         "k_pages": [[[[LN3], [100.0]]], [[[0.0], [LN2]]], [[[5.0], [5.0]]]],
+         "v_pages": [[[[2.0], [1000.0]]], [[[6.0], [0.0]]], [[[50.0], [50.0]]]],
+         "block_table": [[1, 0], [2, 1]], "lens": [3, 1],
+         "out": [[[2.0]], [[50.0]]], "lse": [[math.log(6.0)], [5.0]]},
+    ],
     "bifurcated_examples": [
         {"name": "context_plus_own_decode_rows",
          "cite": "bifurcated-attention page (linnk.ai), section Tiivistelmä: the context part and the decode part together give exact attention",

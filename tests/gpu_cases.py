@@ -45,3 +45,13 @@ def oracle_decode_rows(q, k, v, lens, rows, scale=None):
         o, l = oracle.attention(qb, kb, vb, None, scale)
         res[(b, g)] = (o[0], l[0])
     return res
+
+
+def sampled_units(w, count, seed):
+    """(sequence, KV head) units of a full-size workload to check one by one:
+    the first, the last, and seeded random ones."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    units = {(0, 0), (w.batch - 1, w.kv_heads - 1)}
+    while len(units) < min(count, w.batch * w.kv_heads):
+        units.add((int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))))
+    return sorted(units)

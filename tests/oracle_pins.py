@@ -12,7 +12,9 @@ AssertionError when the oracle disagrees with:
 * closed forms: one row, equal keys, two rows, a dominant score;
 * invariants the pages' exactness claims imply: independence of the split,
   bifurcated = split into context and decode pieces, GQA = MHA with repeated
-  KV, row permutation, shift and linearity in V, convex hull, lse value.
+  KV, row permutation, shift and linearity in V, convex hull, lse value;
+* paged = dense attention on a cache scattered into a shuffled, poisoned
+  page pool by an independently written inverse of the page layout.
 """
 
 import decimal
@@ -51,6 +53,11 @@ def pin_golden(orc):
     for e in ex["combine_examples"]:
         lp = np.array([[(-np.inf if x is None else x) for x in row] for row in e["lse_part"]])
         out, lse = orc.lse_combine(np.array(e["o_part"]), lp)
+        _close(out, e["out"], 1e-12, e["name"] + " out")
+        _close(lse, e["lse"], 1e-12, e["name"] + " lse")
+    for e in ex["paged_examples"]:
+        out, lse = orc.paged_attention(np.array(e["q"]), np.array(e["k_pages"]), np.array(e["v_pages"]),
+                                       np.array(e["block_table"]), np.array(e["lens"]), e["scale"])
         _close(out, e["out"], 1e-12, e["name"] + " out")
         _close(lse, e["lse"], 1e-12, e["name"] + " lse")
     for e in ex["bifurcated_examples"]:
@@ -274,6 +281,50 @@ def pin_row_and_value_invariants(orc):
     _close(l6, l7, 1e-13, "q scale vs temperature lse")
 
 
+def scatter_to_pages(k, v, lens, page_size, extra_pages, seed):
+    """Place a dense cache [B, Hkv, L, D] into a shuffled page pool.
+
+    The inverse of the paged layout, written independently of the oracle:
+    sequence b's j-th block of page_size rows goes to a randomly chosen page.
+    Rows past lens[b] inside a used page, every unused page and every unused
+    table entry are poisoned (NaN rows, page id -1), so any read outside the
+    valid rows shows up.  Returns (k_pages, v_pages, block_table).
+    """
+    B, Hkv, L, D = k.shape
+    per_seq = -(-L // page_size)
+    n_pages = B * per_seq + extra_pages
+    order = np.random.Generator(np.random.PCG64(seed)).permutation(n_pages)
+    kp = np.full((n_pages, Hkv, page_size, D), np.nan)
+    vp = np.full((n_pages, Hkv, page_size, D), np.nan)
+    table = np.full((B, per_seq + 1), -1, dtype=np.int64)
+    used = 0
+    for b in range(B):
+        n = int(lens[b])
+        for j in range(-(-n // page_size)):
+            page = int(order[used])
+            used += 1
+            table[b, j] = page
+            r0, r1 = j * page_size, min((j + 1) * page_size, n)
+            kp[page, :, :r1 - r0] = k[b, :, r0:r1]
+            vp[page, :, :r1 - r0] = v[b, :, r0:r1]
+    return kp, vp, table
+
+
+def pin_paged_is_dense_attention(orc):
+    # [MW] PagedAttention: the table only relocates rows; the result is the
+    # dense result on the same rows, and no poisoned row or entry is read.
+    for seed, (B, Hq, Hkv, D, L, P) in enumerate([(3, 4, 2, 8, 37, 4), (2, 3, 1, 5, 16, 16),
+                                                  (2, 2, 2, 4, 9, 1), (4, 8, 4, 6, 50, 3)]):
+        q = _rand((B, Hq, D), 120 + seed)
+        k, v = _rand((B, Hkv, L, D), 130 + seed), _rand((B, Hkv, L, D), 140 + seed)
+        lens = np.array([L - 7 * b if L - 7 * b > 0 else 1 for b in range(B)])
+        kp, vp, table = scatter_to_pages(k, v, lens, P, extra_pages=3, seed=150 + seed)
+        out, lse = orc.paged_attention(q, kp, vp, table, lens, 0.3)
+        ref_out, ref_lse = orc.attention(q, k, v, lens, 0.3)
+        _close(out, ref_out, 0.0, f"paged case {seed} out")
+        _close(lse, ref_lse, 0.0, f"paged case {seed} lse")
+
+
 ALL_PINS = [pin_golden, pin_decimal_bruteforce, pin_torch_sdpa, pin_closed_forms,
             pin_split_independence, pin_bifurcated_split, pin_gqa_is_repeated_mha,
-            pin_row_and_value_invariants]
+            pin_row_and_value_invariants, pin_paged_is_dense_attention]

@@ -131,6 +131,40 @@ def test_decode_rejects_before_any_hip_call(lib, kw, status):
     assert lib.fd_last_error_message().decode()
 
 
+def _paged(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=None, B=2, Hq=8, Hkv=2, D=128, ps=16, n_pages=64, mp=32,
+             dtype=fd.FD_BF16, n_splits=4, out=FAKE, out_dtype=fd.FD_BF16, lse=None, scale=0.0, ws=FAKE,
+             ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.fd_decode_attn_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                    a["ps"], a["n_pages"], a["mp"], a["dtype"], a["n_splits"], a["out"],
+                                    a["out_dtype"], a["lse"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), fd.FD_ERR_INVALID_ARG),
+    (dict(bt=0x10002), fd.FD_ERR_INVALID_ARG),
+    (dict(k=None), fd.FD_ERR_INVALID_ARG),
+    (dict(v=MISALIGNED), fd.FD_ERR_INVALID_ARG),
+    (dict(ps=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(ps=48), fd.FD_ERR_UNSUPPORTED),
+    (dict(ps=1 << 21), fd.FD_ERR_UNSUPPORTED),
+    (dict(n_pages=0), fd.FD_ERR_INVALID_ARG),
+    (dict(n_pages=1 << 31), fd.FD_ERR_INVALID_ARG),
+    (dict(mp=0), fd.FD_ERR_INVALID_ARG),
+    (dict(mp=1 << 27, ps=16), fd.FD_ERR_INVALID_ARG),     # 2^31 rows per sequence
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=7), fd.FD_ERR_UNSUPPORTED),
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=None), fd.FD_ERR_WORKSPACE),
+    (dict(ws_bytes=64), fd.FD_ERR_WORKSPACE),
+])
+def test_paged_rejects_before_any_hip_call(lib, kw, status):
+    st = _paged(lib, **kw)
+    assert st == status, (st, fd.load().fd_last_error_message())
+    assert lib.fd_last_error_message().decode()
+
+
 def test_bifurcated_rejects_bad_arguments(lib):
     def call(**kw):
         a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=FAKE, vd=FAKE, dl=None, S=4, Hq=8, Hkv=2, D=128, Lc=64, Ld=8,

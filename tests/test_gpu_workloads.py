@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_cases import max_abs, oracle_decode_rows, to_host
+from tests.gpu_cases import max_abs, oracle_decode_rows, sampled_units, to_host
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -31,14 +31,6 @@ def make_decode(w, pad_nan=True):
             k[b, :, n:] = float("nan")
             v[b, :, n:] = float("nan")
     return q, k, v, lens
-
-
-def sampled_units(w, count, seed):
-    rng = np.random.Generator(np.random.PCG64(seed))
-    units = {(0, 0), (w.batch - 1, w.kv_heads - 1)}
-    while len(units) < min(count, w.batch * w.kv_heads):
-        units.add((int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))))
-    return sorted(units)
 
 
 @pytest.mark.parametrize("w", [configs.TINY, configs.CODELLAMA34B_SHARE] + list(configs.MHA_SWEEP),

@@ -24,7 +24,7 @@ def _mutant(**overrides):
     ns = types.SimpleNamespace(
         attention=oa.attention, bifurcated_attention=oa.bifurcated_attention,
         split_partials=oa.split_partials, lse_combine=oa.lse_combine,
-        default_scale=oa.default_scale)
+        default_scale=oa.default_scale, paged_attention=oa.paged_attention)
     for name, fn in overrides.items():
         setattr(ns, name, fn)
     return ns
@@ -44,7 +44,7 @@ def _with_rows(rows_fn):
         return inner
 
     return _mutant(attention=wrap(oa.attention), bifurcated_attention=wrap(oa.bifurcated_attention),
-                   split_partials=wrap(oa.split_partials))
+                   split_partials=wrap(oa.split_partials), paged_attention=wrap(oa.paged_attention))
 
 
 def _rows_no_scale(q, k, v, scale):
@@ -104,6 +104,50 @@ def _combine_plain_mean(o_part, lse_part):
     return o, lse_part.max(axis=0)
 
 
+def _paged_gather(mapping):
+    """paged_attention with the row -> (page, slot) mapping replaced."""
+    def paged(q, k_pages, v_pages, block_table, lens=None, scale=None):
+        k_pages, v_pages = np.asarray(k_pages, np.float64), np.asarray(v_pages, np.float64)
+        table = np.asarray(block_table)
+        B = table.shape[0]
+        P = k_pages.shape[2]
+        Lmax = table.shape[1] * P
+        lens = np.full(B, Lmax) if lens is None else np.asarray(lens)
+        D = k_pages.shape[3]
+        k = np.full((B, k_pages.shape[1], Lmax, D), np.nan)
+        v = np.full_like(k, np.nan)
+        for b in range(B):
+            for t in range(int(lens[b])):
+                page, slot, head_axis_swapped = mapping(table, b, t, P)
+                if head_axis_swapped:
+                    # pages read as [P, Hkv, D] instead of [Hkv, P, D]
+                    Hkv = k.shape[1]
+                    k[b, :, t] = k_pages[page].reshape(-1, D)[slot * Hkv: (slot + 1) * Hkv]
+                    v[b, :, t] = v_pages[page].reshape(-1, D)[slot * Hkv: (slot + 1) * Hkv]
+                else:
+                    k[b, :, t] = k_pages[page, :, slot]
+                    v[b, :, t] = v_pages[page, :, slot]
+        return oa.attention(q, k, v, lens, scale)
+    return paged
+
+
+def _map_page_slot_swapped(table, b, t, P):
+    return table[b, t % P], t // P, False
+
+
+def _map_table_transposed(table, b, t, P):
+    return table.T.reshape(table.shape)[b, t // P], t % P, False
+
+
+def _map_head_axis_swapped(table, b, t, P):
+    return table[b, t // P], t % P, True
+
+
+def _map_whole_last_page(table, b, t, P):
+    # reads the page of row t but always from slot P - 1 of the last page
+    return table[b, t // P], (t % P if t + P < table.shape[1] * P else P - 1), False
+
+
 MUTANTS = {
     "dropped_scale": lambda: _with_rows(_rows_no_scale),
     "lse_in_log2": lambda: _with_rows(_rows_log2_lse),
@@ -114,6 +158,10 @@ MUTANTS = {
     "interleaved_gqa": lambda: _mutant(attention=_attention_interleaved_gqa),
     "combine_wrong_sign": lambda: _mutant(lse_combine=_combine_wrong_sign),
     "combine_unweighted": lambda: _mutant(lse_combine=_combine_plain_mean),
+    "paged_page_slot_swapped": lambda: _mutant(paged_attention=_paged_gather(_map_page_slot_swapped)),
+    "paged_table_transposed": lambda: _mutant(paged_attention=_paged_gather(_map_table_transposed)),
+    "paged_head_axis_swapped": lambda: _mutant(paged_attention=_paged_gather(_map_head_axis_swapped)),
+    "paged_wrong_slot_in_tail": lambda: _mutant(paged_attention=_paged_gather(_map_whole_last_page)),
 }
 
 
@@ -131,6 +179,6 @@ def test_pins_catch_planted_mistake(name):
     for pin in pins.ALL_PINS:
         try:
             pin(orc)
-        except (AssertionError, ValueError, FloatingPointError):
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake {name}"

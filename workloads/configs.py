@@ -7,7 +7,8 @@ seed k for its tensors; point j of a sweep uses 100*k + j.
 from dataclasses import dataclass
 
 __all__ = ["DecodeWorkload", "BifurcatedWorkload", "TINY", "CODELLAMA34B_SHARE",
-           "MHA_SWEEP", "BIFURCATED_MQA", "BIFURCATED_GQA", "ALL_DECODE", "ALL_BIFURCATED"]
+           "MHA_SWEEP", "BIFURCATED_MQA", "BIFURCATED_GQA", "CODELLAMA34B_SHARE_PAGED",
+           "MHA_B16_L65536_PAGED", "ALL_DECODE", "ALL_BIFURCATED", "ALL_PAGED"]
 
 
 @dataclass(frozen=True)
@@ -23,6 +24,7 @@ class DecodeWorkload:
     n_splits: int              # <= 0: split count chosen by the planner
     seed: int
     tol: float                 # max-abs error bound against the fp64 oracle
+    page_size: int = 0         # > 0: paged cache of pages this many rows long
 
     def kv_bytes_allocated(self):
         sz = 2 if self.dtype == "bf16" else 4
@@ -72,5 +74,13 @@ BIFURCATED_MQA = BifurcatedWorkload("bifurcated_mqa_s64_ctx8192_dec256_hq32_hkv1
 BIFURCATED_GQA = BifurcatedWorkload("bifurcated_gqa_s128_ctx32768_dec1to512_hq32_hkv8_d128_bf16",
                                     128, 32, 8, 128, 32768, 512, 1, "bf16", 5, 1e-2)
 
+# Paged-cache forms of the 64K workloads: the same shapes with the cache in
+# 16-row pages (a common serving block size) handed out in shuffled order.
+CODELLAMA34B_SHARE_PAGED = DecodeWorkload("codellama34b_share_paged16_b1_hq16_hkv2_d128_l65536_bf16",
+                                          1, 16, 2, 128, 65536, "bf16", False, 0, 6, 1e-2, page_size=16)
+MHA_B16_L65536_PAGED = DecodeWorkload("mha_paged16_b16_h32_d128_l65536_bf16", 16, 32, 32, 128, 65536,
+                                      "bf16", True, 0, 7, 1e-2, page_size=16)
+
 ALL_DECODE = (TINY, CODELLAMA34B_SHARE) + MHA_SWEEP
+ALL_PAGED = (CODELLAMA34B_SHARE_PAGED, MHA_B16_L65536_PAGED)
 ALL_BIFURCATED = (BIFURCATED_MQA, BIFURCATED_GQA)

@@ -20,6 +20,8 @@ __all__ = [
     "bifurcated_case",
     "device_normal",
     "device_lengths",
+    "paginate",
+    "shuffled_block_table",
 ]
 
 
@@ -127,3 +129,42 @@ def device_lengths(count, lo, hi, seed, device):
     import torch
 
     return torch.tensor(host_lengths(count, lo, hi, seed), dtype=torch.int32, device=device)
+
+
+def shuffled_block_table(batch, pages_per_seq, seed, first_page=1):
+    """Page ids for a paged cache: sequence b's j-th page is entry [b, j].
+
+    The batch * pages_per_seq pages first_page, first_page + 1, ... are
+    handed out in an order shuffled by PCG64(seed), as a pool allocator that
+    has served many sequences would.  Returns int32 [batch, pages_per_seq].
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    ids = first_page + g.permutation(batch * pages_per_seq)
+    return ids.reshape(batch, pages_per_seq).astype(np.int32)
+
+
+def paginate(k, v, lens, page_size, seed):
+    """A dense host cache [B, Hkv, L, D] laid out as a shuffled page pool.
+
+    Returns (k_pages, v_pages [n_pages, Hkv, page_size, D], block_table
+    [B, ceil(L / page_size) + 1] int32).  Page 0 is never handed out and is
+    filled with NaN; table entries past a sequence's last page hold -1; rows
+    past lens[b] inside a used page keep the dense cache's padding.  Only
+    data movement: rows are copied, never combined.
+    """
+    B, Hkv, L, D = k.shape
+    per_seq = -(-L // page_size)
+    ids = shuffled_block_table(B, per_seq, seed)
+    n_pages = 1 + B * per_seq
+    kp = np.full((n_pages, Hkv, page_size, D), np.nan, dtype=np.float32)
+    vp = np.full((n_pages, Hkv, page_size, D), np.nan, dtype=np.float32)
+    table = np.full((B, per_seq + 1), -1, dtype=np.int32)
+    for b in range(B):
+        used = -(-int(lens[b]) // page_size)
+        for j in range(used):
+            page = int(ids[b, j])
+            table[b, j] = page
+            r0, r1 = j * page_size, min((j + 1) * page_size, L)
+            kp[page, :, :r1 - r0] = k[b, :, r0:r1]
+            vp[page, :, :r1 - r0] = v[b, :, r0:r1]
+    return kp, vp, table
