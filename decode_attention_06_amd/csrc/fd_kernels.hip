@@ -127,12 +127,14 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
     }
 
-    // Dense: the (b, kvh) slice's first row.  Paged: the pool; rows are
-    // found per 16-row group (a wave's tile covers NG groups; the row of
-    // load u lies in group u * RPW / 16).
+    // Rows are addressed per 16-row group: a wave-uniform 64-bit base (the
+    // dense slice's row, or the row's page) plus a 32-bit lane offset below
+    // 16 * D * sizeof(T), so each load takes one offset register.  A wave
+    // tile covers NG groups; the rows of load u lie in group u * RPW / 16.
+    const char* kpool = static_cast<const char*>(p.k);
+    const char* vpool = static_cast<const char*>(p.v);
     const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
-    const T* kb = static_cast<const T*>(p.k) + slice + c * EPL;
-    const T* vb = static_cast<const T*>(p.v) + slice + c * EPL;
+    const uint32_t lane_off = c * EPL * (uint32_t)sizeof(T);
     constexpr int NG = WAVE_TOK >= 16 ? WAVE_TOK / 16 : 1;
     static_assert(16 % RPW == 0, "a load's rows must stay inside one 16-row group");
 
@@ -145,37 +147,46 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
 
-    for (int tb = t0 + wave * WAVE_TOK; tb < t1; tb += WG_TOK) {
-        const bool full = tb + WAVE_TOK <= t1;
-        // Unconditional loads; rows at or beyond t1 clamp to t1 - 1 (a valid
-        // row whose score is masked below), so the loads issue back to back.
-        uint4 kr[U], vr[U];
-        if constexpr (PAGED) {
-            const int last = t1 - 1;
-            int gs[NG];
-            int64_t go[NG];
+    // Paged: first rows and page ids of the 16-row groups of the next tile
+    // to load (scalar loads, issued one tile ahead of their use).
+    int gs[NG], gid[NG];
+    auto lookup = [&](int at) {
 #pragma unroll
-            for (int h = 0; h < NG; ++h) {
-                gs[h] = kv_group_start(tb + 16 * h, last);
-                go[h] = kv_row_offset<true, D>(p, b, kvh, gs[h]);
-            }
+        for (int h = 0; h < NG; ++h) {
+            gs[h] = kv_group_start(at + 16 * h, t1 - 1);
+            gid[h] = kv_page_id(p, b, gs[h]);
+        }
+    };
+
+    // Loads one wave tile starting at row tb.  Unconditional: rows at or
+    // beyond t1 clamp to t1 - 1 (a valid row, masked in compute), so the
+    // loads issue back to back and a prefetch past the piece's end only
+    // re-reads that row.
+    auto load = [&](int tb, uint4 (&kr)[U], uint4 (&vr)[U]) {
+        int64_t gb[NG];   // bytes from the pool to row gs[h]
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int h = (NG > 1) ? (u * RPW) / 16 : 0;
-                const int t = min(tb + u * RPW + r, last);
-                const int64_t off = go[h] + (int64_t)(t - gs[h]) * D;
-                kr[u] = *reinterpret_cast<const uint4*>(kb + off);
-                vr[u] = *reinterpret_cast<const uint4*>(vb + off);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int t = min(tb + u * RPW + r, t1 - 1);
-                kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)t * D);
-                vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)t * D);
+        for (int h = 0; h < NG; ++h) {
+            if constexpr (PAGED) {
+                gb[h] = kv_page_offset<D>(p, gid[h], kvh, gs[h]) * (int64_t)sizeof(T);
+            } else {
+                gs[h] = kv_group_start(tb + 16 * h, t1 - 1);
+                gb[h] = (slice + (int64_t)gs[h] * D) * (int64_t)sizeof(T);
             }
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int h = (NG > 1) ? (u * RPW) / 16 : 0;
+            const int t = min(tb + u * RPW + r, t1 - 1);
+            const uint32_t off = (uint32_t)(t - gs[h]) * (uint32_t)(D * sizeof(T)) + lane_off;
+            kr[u] = *reinterpret_cast<const uint4*>(kpool + gb[h] + off);
+            vr[u] = *reinterpret_cast<const uint4*>(vpool + gb[h] + off);
+        }
+        if constexpr (PAGED) lookup(tb + WG_TOK);
+    };
 
+    // Scores, online-softmax update and P.V for one loaded wave tile.
+    auto compute = [&](int tb, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+        const bool full = tb + WAVE_TOK <= t1;
         // Scores (log2 domain).  All lanes take part in the DPP sums.
         float s[U][GB];
 #pragma unroll
@@ -228,6 +239,45 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[u][g], vf[e], acc[g][e]);
         }
+    };
+
+    // Two register buffers, both in flight before the loop: each tile is
+    // computed, then its buffer is refilled with the tile after next, so the
+    // other buffer's loads stay in flight across every compute.  A counted
+    // loop over tile pairs with one exit keeps each buffer in its registers
+    // across the back edge; the scheduling barriers keep each refill after
+    // the compute that frees its registers and ahead of the next compute's
+    // waits.
+    // Eight query rows per unit leave no registers for a second buffer.
+    const int tb0 = t0 + wave * WAVE_TOK;
+    if (GB >= 8) {
+        if (tb0 < t1) {
+            if constexpr (PAGED) lookup(tb0);
+            uint4 ka[U], va[U];
+            for (int tb = tb0; tb < t1; tb += WG_TOK) {
+                load(tb, ka, va);
+                compute(tb, ka, va);
+            }
+        }
+    } else if (tb0 < t1) {
+        const int ntiles = (t1 - tb0 + WG_TOK - 1) / WG_TOK;
+        uint4 ka[U], va[U], kn[U], vn[U];
+        if constexpr (PAGED) lookup(tb0);
+        load(tb0, ka, va);
+        load(tb0 + WG_TOK, kn, vn);
+        int tb = tb0;
+        for (int it = 0; it < ntiles / 2; ++it) {
+            compute(tb, ka, va);
+            __builtin_amdgcn_sched_barrier(0);
+            load(tb + 2 * WG_TOK, ka, va);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(tb + WG_TOK, kn, vn);
+            __builtin_amdgcn_sched_barrier(0);
+            load(tb + 3 * WG_TOK, kn, vn);
+            __builtin_amdgcn_sched_barrier(0);
+            tb += 2 * WG_TOK;
+        }
+        if (ntiles & 1) compute(tb, ka, va);
     }
 
     // Merge the RPW row groups of the wave (butterfly across lane offsets

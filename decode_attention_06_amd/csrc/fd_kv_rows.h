@@ -17,14 +17,25 @@
 
 namespace fd {
 
+// The two halves of kv_row_offset<true>: the table entry of row t (a
+// scalar load; issued early, its latency hides behind other work) and the
+// element offset that entry gives, computed where it is used.
+__device__ __forceinline__ int kv_page_id(const PartialParams& p, int b, int t) {
+    return p.block_table[(int64_t)b * p.bt_stride + (t >> p.page_shift)];
+}
+
+template <int D>
+__device__ __forceinline__ int64_t kv_page_offset(const PartialParams& p, int page, int kvh, int t) {
+    page = min(max(page, 0), p.n_pages - 1);
+    const int in_page = t & ((1 << p.page_shift) - 1);
+    return (int64_t)page * p.page_stride + (int64_t)kvh * p.kv_stride_h + (int64_t)in_page * D;
+}
+
 // Element offset of row t (any row of its 16-row group) of (b, kvh).
 template <bool PAGED, int D>
 __device__ __forceinline__ int64_t kv_row_offset(const PartialParams& p, int b, int kvh, int t) {
     if constexpr (PAGED) {
-        int page = p.block_table[(int64_t)b * p.bt_stride + (t >> p.page_shift)];
-        page = min(max(page, 0), p.n_pages - 1);
-        const int in_page = t & ((1 << p.page_shift) - 1);
-        return (int64_t)page * p.page_stride + (int64_t)kvh * p.kv_stride_h + (int64_t)in_page * D;
+        return kv_page_offset<D>(p, kv_page_id(p, b, t), kvh, t);
     } else {
         return (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + (int64_t)t * D;
     }

@@ -37,33 +37,47 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
     }
 }
 
-// Paged form of load_tile: the tile (16-row aligned) covers two 16-row
-// groups, each inside one page.  A lane's K rows lie in group i / 8 and its
-// V rows in group g / 2; rows at or beyond t1 clamp to t1 - 1 as above, and
-// kv_group_start gives the group that then holds them.
-__device__ __forceinline__ void load_tile_paged(const PartialParams& p, int b, int kvh, int tb, int t1,
-                                                int ktok0, int g, int i, u32x4_t (&kr)[2][4],
-                                                u32x4_t (&vr)[8]) {
+// Paged tiles.  A tile (16-row aligned) covers two 16-row groups, each
+// inside one page: PagedTile holds their first rows and element offsets
+// (wave-uniform; the page ids come from scalar loads, looked up one tile
+// ahead so that their latency hides behind the current tile's work).
+struct PagedTile {
+    int s0, s1;       // first rows of the two groups
+    int id0, id1;     // their page ids (table entries)
+};
+
+__device__ __forceinline__ PagedTile paged_tile(const PartialParams& p, int b, int tb, int last) {
+    PagedTile r;
+    r.s0 = kv_group_start(tb, last);
+    r.s1 = kv_group_start(tb + 16, last);
+    r.id0 = kv_page_id(p, b, r.s0);
+    r.id1 = kv_page_id(p, b, r.s1);
+    return r;
+}
+
+// Paged form of load_tile.  A lane's K rows lie in group i / 8 and its V
+// rows in group g / 2; rows at or beyond t1 clamp to t1 - 1 as above, and
+// kv_group_start gave the group that then holds them.
+__device__ __forceinline__ void load_tile_paged(const PartialParams& p, int kvh, const uint16_t* kpool,
+                                                const uint16_t* vpool, const PagedTile& r, int tb, int t1,
+                                                int ktok0, int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
     const int last = t1 - 1;
-    const int s0 = kv_group_start(tb, last), s1 = kv_group_start(tb + 16, last);
-    const int64_t o0 = kv_row_offset<true, MF_D>(p, b, kvh, s0);
-    const int64_t o1 = kv_row_offset<true, MF_D>(p, b, kvh, s1);
-    const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
-    const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
+    const int64_t o0 = kv_page_offset<MF_D>(p, r.id0, kvh, r.s0) - (int64_t)r.s0 * MF_D;
+    const int64_t o1 = kv_page_offset<MF_D>(p, r.id1, kvh, r.s1) - (int64_t)r.s1 * MF_D;
     const bool khi = i >= 8, vhi = g >= 2;
-    const uint16_t* kg = kpool + (khi ? o1 : o0) - (int64_t)(khi ? s1 : s0) * MF_D + 8 * g;
-    const uint16_t* vg = vpool + (vhi ? o1 : o0) - (int64_t)(vhi ? s1 : s0) * MF_D + 8 * i;
+    const int64_t ko = (khi ? o1 : o0) + 8 * g;
+    const int64_t vo = (vhi ? o1 : o0) + 8 * i;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int t = min(tb + ktok0 + 4 * blk, last);
-        const uint16_t* src = kg + (int64_t)t * MF_D;
+        const uint16_t* src = kpool + ko + (int64_t)t * MF_D;
 #pragma unroll
         for (int s = 0; s < 4; ++s) kr[blk][s] = ld16(src + 32 * s);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = min(tb + 8 * g + j, last);
-        vr[j] = ld16(vg + (int64_t)t * MF_D);
+        vr[j] = ld16(vpool + vo + (int64_t)t * MF_D);
     }
 }
 
@@ -144,14 +158,19 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // before each tile covers only that tile's own loads.
     constexpr int STEP = NW * MF_TILE;
     u32x4_t ka[2][4], va[8], kb2[2][4], vb2[8];
+    // Paged: `ahead` holds the page offsets of the next tile to load.
+    PagedTile ahead{};
     auto load = [&](int at, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
-        if constexpr (PAGED)
-            load_tile_paged(p, b, kvh, at, t1, ktok0, g, i, kr, vr);
-        else
+        if constexpr (PAGED) {
+            load_tile_paged(p, kvh, kbase, vbase, ahead, at, t1, ktok0, g, i, kr, vr);
+            ahead = paged_tile(p, b, at + STEP, t1 - 1);
+        } else {
             load_tile(kbase, vbase, at, t1, ktok0, g, i, kr, vr);
+        }
     };
     int tb = t0 + wave * MF_TILE;
     if (tb < t1) {
+        if constexpr (PAGED) ahead = paged_tile(p, b, tb, t1 - 1);
         load(tb, ka, va);
         while (true) {
             load(tb + STEP, kb2, vb2);
