@@ -6,8 +6,10 @@ import this package; the HIP library and its Python binding never do.
 
 from .fp64 import (  # noqa: F401
     attention,
+    attention_fp8kv,
     bifurcated_attention,
     default_scale,
+    fp8_e4m3_value,
     lse_combine,
     paged_attention,
     split_partials,

@@ -54,6 +54,8 @@ __all__ = [
     "split_partials",
     "lse_combine",
     "paged_attention",
+    "fp8_e4m3_value",
+    "attention_fp8kv",
 ]
 
 
@@ -177,6 +179,45 @@ def paged_attention(q, k_pages, v_pages, block_table, lens=None, scale=None):
             out[b, rows] = o
             lse[b, rows] = l
     return out, lse
+
+
+def fp8_e4m3_value(bits):
+    """Values of OCP 8-bit floating-point E4M3 codes (the "fn" variant).
+
+    Bit layout s eeee mmm, exponent bias 7.  Exponent field 0 holds the
+    subnormals m/8 * 2^-6 (and +-0); otherwise the value is
+    (1 + m/8) * 2^(e - 7).  The codes with every exponent and mantissa bit
+    set (0x7F, 0xFF) are NaN; there are no infinities, so the largest finite
+    magnitude is 1.75 * 2^8 = 448.
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFF
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def attention_fp8kv(q, k_bits, v_bits, k_scale=None, v_scale=None, lens=None, scale=None):
+    """Decode attention over an 8-bit E4M3 KV cache with per-KV-head scales.
+
+    q               [B, Hq, D] values
+    k_bits, v_bits  [B, Hkv, Lmax, D] E4M3 codes
+    k_scale, v_scale  [Hkv] (None: 1); cache row value = code value * scale
+    [MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", quantisation paragraph:
+    fewer bits per stored value move fewer bytes over the memory bus.  The
+    codes follow the OCP 8-bit floating-point specification (E4M3, see
+    fp8_e4m3_value); the attention is the plain attention over the
+    dequantised cache.
+    """
+    k_bits = np.asarray(k_bits)
+    Hkv = k_bits.shape[1]
+    ks = np.ones(Hkv) if k_scale is None else _as_f64(k_scale)
+    vs = np.ones(Hkv) if v_scale is None else _as_f64(v_scale)
+    k = fp8_e4m3_value(k_bits) * ks[None, :, None, None]
+    v = fp8_e4m3_value(v_bits) * vs[None, :, None, None]
+    return attention(q, k, v, lens, scale)
 
 
 def bifurcated_attention(q, k_ctx, v_ctx, k_dec, v_dec, dec_lens=None, scale=None):

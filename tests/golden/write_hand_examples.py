@@ -65,6 +65,14 @@ EXAMPLES = {
          "block_table": [[1, 0], [2, 1]], "lens": [3, 1],
          "out": [[[2.0]], [[50.0]]], "lse": [[math.log(6.0)], [5.0]]},
     ],
+    "fp8kv_examples": [
+        {"name": "e4m3_codes_with_head_scales",
+         "cite": "memory-wall page (gyaansetu.com), section on fighting the memory wall, quantisation paragraph: fewer bits per stored value; E4M3 codes as defined by the OCP 8-bit floating-point specification (bias 7)",
+         "derivation": "K codes 0x00 = 0 and 0x38 = 1.0 with k_scale ln 3 -> scores 0 and ln 3 -> weights 1:3. V codes 0x40 = 2.0 and 0x48 = 4.0 with v_scale 1/2 -> values 1 and 2 -> out = (1 + 3*2)/4 = 7/4; lse = ln 4",
+         "scale": 1.0, "q": [[[1.0]]], "k_bits": [[[[0], [56]]]], "v_bits": [[[[64], [72]]]],
+         "k_scale": [LN3], "v_scale": [0.5], "lens": [2],
+         "out": [[[1.75]]], "lse": [[LN4]]},
+    ],
     "bifurcated_examples": [
         {"name": "context_plus_own_decode_rows",
          "cite": "bifurcated-attention page (linnk.ai), section Tiivistelmä: the context part and the decode part together give exact attention",

@@ -14,7 +14,10 @@ AssertionError when the oracle disagrees with:
   bifurcated = split into context and decode pieces, GQA = MHA with repeated
   KV, row permutation, shift and linearity in V, convex hull, lse value;
 * paged = dense attention on a cache scattered into a shuffled, poisoned
-  page pool by an independently written inverse of the page layout.
+  page pool by an independently written inverse of the page layout;
+* E4M3 code values against torch's float8_e4m3fn decoder and hand-worked
+  landmarks; fp8-cache attention = dense attention on the values that
+  decoder gives, times the per-head scales.
 """
 
 import decimal
@@ -58,6 +61,12 @@ def pin_golden(orc):
     for e in ex["paged_examples"]:
         out, lse = orc.paged_attention(np.array(e["q"]), np.array(e["k_pages"]), np.array(e["v_pages"]),
                                        np.array(e["block_table"]), np.array(e["lens"]), e["scale"])
+        _close(out, e["out"], 1e-12, e["name"] + " out")
+        _close(lse, e["lse"], 1e-12, e["name"] + " lse")
+    for e in ex["fp8kv_examples"]:
+        out, lse = orc.attention_fp8kv(np.array(e["q"]), np.array(e["k_bits"]), np.array(e["v_bits"]),
+                                       np.array(e["k_scale"]), np.array(e["v_scale"]), np.array(e["lens"]),
+                                       e["scale"])
         _close(out, e["out"], 1e-12, e["name"] + " out")
         _close(lse, e["lse"], 1e-12, e["name"] + " lse")
     for e in ex["bifurcated_examples"]:
@@ -325,6 +334,46 @@ def pin_paged_is_dense_attention(orc):
         _close(lse, ref_lse, 0.0, f"paged case {seed} lse")
 
 
+def pin_fp8_codes(orc):
+    # every E4M3 code against torch's float8_e4m3fn (a library decoder) ...
+    import torch
+
+    codes = np.arange(256)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = orc.fp8_e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "fp8 NaN codes"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]), "fp8 code values"
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin])), "fp8 signed zeros"
+    # ... and against the format's landmarks, worked by hand
+    for code, val in ((0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),
+                      (0x08, 2.0 ** -6), (0x40, 2.0), (0xC0, -2.0), (0x3C, 1.5)):
+        assert orc.fp8_e4m3_value(np.array([code]))[0] == val, f"fp8 code {code:#x}"
+
+
+def pin_fp8_attention_is_dense_attention(orc):
+    # dequantising with torch's decoder and per-head scales, then plain attention
+    import torch
+
+    B, Hq, Hkv, D, L = 2, 8, 2, 16, 40
+    rng = np.random.Generator(np.random.PCG64(160))
+    kb = rng.integers(0, 256, size=(B, Hkv, L, D))
+    vb = rng.integers(0, 256, size=(B, Hkv, L, D))
+    kb[(kb & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    vb[(vb & 0x7F) == 0x7F] = 0x30
+    q = _rand((B, Hq, D), 161, 0.05)
+    ks, vs = np.array([0.02, 0.005]), np.array([1.5, 0.25])
+    lens = np.array([40, 23])
+    dec = lambda c: torch.from_numpy(c.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    k = dec(kb) * ks[None, :, None, None]
+    v = dec(vb) * vs[None, :, None, None]
+    out, lse = orc.attention_fp8kv(q, kb, vb, ks, vs, lens, 0.3)
+    ref_out, ref_lse = orc.attention(q, k, v, lens, 0.3)
+    _close(out, ref_out, 0.0, "fp8 kv out")
+    _close(lse, ref_lse, 0.0, "fp8 kv lse")
+
+
 ALL_PINS = [pin_golden, pin_decimal_bruteforce, pin_torch_sdpa, pin_closed_forms,
             pin_split_independence, pin_bifurcated_split, pin_gqa_is_repeated_mha,
-            pin_row_and_value_invariants, pin_paged_is_dense_attention]
+            pin_row_and_value_invariants, pin_paged_is_dense_attention, pin_fp8_codes,
+            pin_fp8_attention_is_dense_attention]

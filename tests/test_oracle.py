@@ -24,7 +24,8 @@ def _mutant(**overrides):
     ns = types.SimpleNamespace(
         attention=oa.attention, bifurcated_attention=oa.bifurcated_attention,
         split_partials=oa.split_partials, lse_combine=oa.lse_combine,
-        default_scale=oa.default_scale, paged_attention=oa.paged_attention)
+        default_scale=oa.default_scale, paged_attention=oa.paged_attention,
+        fp8_e4m3_value=oa.fp8_e4m3_value, attention_fp8kv=oa.attention_fp8kv)
     for name, fn in overrides.items():
         setattr(ns, name, fn)
     return ns
@@ -148,6 +149,32 @@ def _map_whole_last_page(table, b, t, P):
     return table[b, t // P], (t % P if t + P < table.shape[1] * P else P - 1), False
 
 
+def _fp8_bias8(bits):
+    # exponent bias 8 (the FNUZ variant's) instead of 7
+    return oa.fp8_e4m3_value(bits) / 2.0
+
+
+def _fp8_no_subnormals(bits):
+    b = np.asarray(bits).astype(np.int64) & 0xFF
+    v = oa.fp8_e4m3_value(bits)
+    return np.where((b & 0x78) == 0, np.where(b >> 7, -1.0, 1.0) * (1 + (b & 7) / 8.0) * 2.0 ** -7, v)
+
+
+def _fp8_with(value_fn):
+    def attn(q, k_bits, v_bits, k_scale=None, v_scale=None, lens=None, scale=None):
+        Hkv = np.asarray(k_bits).shape[1]
+        ks = np.ones(Hkv) if k_scale is None else np.asarray(k_scale, np.float64)
+        vs = np.ones(Hkv) if v_scale is None else np.asarray(v_scale, np.float64)
+        k = value_fn(k_bits) * ks[None, :, None, None]
+        v = value_fn(v_bits) * vs[None, :, None, None]
+        return oa.attention(q, k, v, lens, scale)
+    return attn
+
+
+def _fp8_scales_swapped(q, k_bits, v_bits, k_scale=None, v_scale=None, lens=None, scale=None):
+    return oa.attention_fp8kv(q, k_bits, v_bits, v_scale, k_scale, lens, scale)
+
+
 MUTANTS = {
     "dropped_scale": lambda: _with_rows(_rows_no_scale),
     "lse_in_log2": lambda: _with_rows(_rows_log2_lse),
@@ -162,6 +189,10 @@ MUTANTS = {
     "paged_table_transposed": lambda: _mutant(paged_attention=_paged_gather(_map_table_transposed)),
     "paged_head_axis_swapped": lambda: _mutant(paged_attention=_paged_gather(_map_head_axis_swapped)),
     "paged_wrong_slot_in_tail": lambda: _mutant(paged_attention=_paged_gather(_map_whole_last_page)),
+    "fp8_exponent_bias_8": lambda: _mutant(fp8_e4m3_value=_fp8_bias8, attention_fp8kv=_fp8_with(_fp8_bias8)),
+    "fp8_subnormals_as_normals": lambda: _mutant(fp8_e4m3_value=_fp8_no_subnormals,
+                                                 attention_fp8kv=_fp8_with(_fp8_no_subnormals)),
+    "fp8_scales_swapped": lambda: _mutant(attention_fp8kv=_fp8_scales_swapped),
 }
 
 
