@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATION_BYTES = 1 << 30
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_PAGED + configs.ALL_BIFURCATED)}
+WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_PAGED + configs.ALL_FP8 + configs.ALL_BIFURCATED)}
 DEFAULT_WORKLOAD = configs.CODELLAMA34B_SHARE.name
 
 
@@ -211,22 +211,45 @@ def time_decode(w, steps, warmup, force_splits=0):
     return info, (host, lens.cpu().numpy())
 
 
-def time_paged(w, steps, warmup, force_splits=0):
-    """Decode over a paged cache.  The dominant kernel's time is the step's
-    minus the combine's, the combine timed alone on the same partials (the
-    paged entry point runs both launches)."""
+def fp8_inputs(w, copies, dev):
+    """E4M3 caches (one per copy) with per-KV-head scales."""
+    import torch
+
+    if w.ragged:
+        lens = synth.device_lengths(w.batch, w.max_len // 2, w.max_len, w.seed + 7, dev)
+    else:
+        lens = torch.full((w.batch,), w.max_len, dtype=torch.int32, device=dev)
+    ks = synth.head_scales(w.kv_heads, w.seed + 3)
+    vs = synth.head_scales(w.kv_heads, w.seed + 4)
+    shape = (w.batch, w.kv_heads, w.max_len, w.head_dim)
+    sets = []
+    for c in range(copies):
+        s = w.seed + 1000 * c
+        q = synth.device_normal((w.batch, w.q_heads, w.head_dim), s, "bf16", dev)
+        sets.append((q, synth.device_fp8(shape, s + 1, ks, dev), synth.device_fp8(shape, s + 2, vs, dev)))
+    return sets, torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev), lens
+
+
+def time_variant(w, steps, warmup, force_splits=0):
+    """Decode over a paged or an E4M3 cache.  The dominant kernel's time is
+    the step's minus the combine's, the combine timed alone on the same
+    partials (these entry points run both launches)."""
     import torch
 
     import decode_attention_06_amd as fd
 
     dev = torch.device("cuda:0")
-    sz = 2 if w.dtype == "bf16" else 4
+    sz = {"bf16": 2, "fp32": 4, "fp8": 1}[w.dtype]
     alloc_bytes = 2 * w.batch * w.kv_heads * w.max_len * w.head_dim * sz
     copies = max(2, math.ceil(ROTATION_BYTES / alloc_bytes))
-    sets, table, lens = paged_inputs(w, copies, dev)
+    if w.dtype == "fp8":
+        sets, ks, vs, lens = fp8_inputs(w, copies, dev)
+        max_len, dt = w.max_len, fd.FD_FP8_E4M3
+    else:
+        sets, table, lens = paged_inputs(w, copies, dev)
+        max_len = table.shape[1] * w.page_size
+        dt = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
     kv_bytes = 2 * int(lens.sum().item()) * w.kv_heads * w.head_dim * sz
-    dt = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
-    max_len = table.shape[1] * w.page_size
     ns = force_splits or (w.n_splits if w.n_splits > 0 else fd.plan_splits(
         w.batch, w.q_heads, w.kv_heads, w.head_dim, max_len, dt, fd.device_cu_count()))
     rows = w.batch * w.q_heads
@@ -235,8 +258,11 @@ def time_paged(w, steps, warmup, force_splits=0):
                      dtype=torch.uint8, device=dev)
 
     def step(j):
-        q, kp, vp = sets[j % copies]
-        fd.decode_attn_paged(q, kp, vp, table, lens, n_splits=ns, out=out, workspace=ws)
+        q, k, v = sets[j % copies]
+        if w.dtype == "fp8":
+            fd.decode_attn_fp8(q, k, v, ks, vs, lens, n_splits=ns, out=out, workspace=ws)
+        else:
+            fd.decode_attn_paged(q, k, v, table, lens, n_splits=ns, out=out, workspace=ws)
 
     for j in range(warmup):
         step(j)
@@ -252,7 +278,7 @@ def time_paged(w, steps, warmup, force_splits=0):
     info = {
         "n_splits": ns, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms,
         "kernel_ms": step_ms - combine_ms, "eager_step_ms": eager_ms, "probe_gbs": None,
-        "kernel": "partial_mfma_kernel" if (w.dtype == "bf16" and w.head_dim == 128 and
+        "kernel": "partial_mfma_kernel" if (w.dtype in ("bf16", "fp8") and w.head_dim == 128 and
                                              w.q_heads // w.kv_heads >= 4) else "partial_valu_kernel",
         "kernel_timing": "step minus the combine timed alone",
         "flops": 4 * int(lens.sum().item()) * w.q_heads * w.head_dim,
@@ -423,9 +449,9 @@ def main():
     if bif:
         info, host = time_bifurcated(w, args.steps, args.warmup, args.compare_concat)
         dtype = w.dtype
-    elif getattr(w, "page_size", 0) > 0:
-        info, host = time_paged(w, args.steps, args.warmup, args.n_splits)
-        dtype = w.dtype
+    elif getattr(w, "page_size", 0) > 0 or w.dtype == "fp8":
+        info, host = time_variant(w, args.steps, args.warmup, args.n_splits)
+        dtype = "fp8_e4m3 cache, bf16 query" if w.dtype == "fp8" else w.dtype
     else:
         info, host = time_decode(w, args.steps, args.warmup, args.n_splits)
         dtype = w.dtype

@@ -13,7 +13,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
-FD_F32, FD_BF16 = 0, 1
+FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
 FD_MAX_SPLITS = 4096
 
 # Exported symbols and their ctypes signatures (mirrors include/fd.h).
@@ -28,6 +28,8 @@ SIGNATURES = {
                                                ctypes.POINTER(_c_sz)]),
     "fd_decode_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                 _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_decode_attn_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
     "fd_decode_attn_paged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32,
                                       _c_vp, _c_sz, _c_vp]),
@@ -163,6 +165,52 @@ def decode_attn(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=
                               B, Hq, Hkv, D, Lmax, dt, int(n_splits), _dev_ptr(out, "out"), _dtype_code(out),
                               _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def _fp8_codes(t, name):
+    torch = _torch()
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise FdError(FD_ERR_UNSUPPORTED, f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    return _dev_ptr(t, name)
+
+
+def decode_attn_fp8(q, k, v, k_scale=None, v_scale=None, lens=None, n_splits=0, out=None, out_dtype=None,
+                    scale=0.0, return_lse=False, workspace=None, stream=None):
+    """Split-KV decode attention over an E4M3 KV cache (fd_decode_attn_fp8).
+
+    q bf16 [B, Hq, D]; k, v [B, Hkv, Lmax, D] E4M3 codes (uint8 or
+    float8_e4m3fn); k_scale, v_scale float32 [Hkv] on the device or None
+    (= 1): cache value = code value * scale of its KV head.
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise FdError(FD_ERR_INVALID_ARG, "expected q [B,Hq,D] and k, v [B,Hkv,Lmax,D]")
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, Dk = k.shape
+    if k.shape[0] != B or Dk != D:
+        raise FdError(FD_ERR_INVALID_ARG, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype != torch.bfloat16:
+        raise FdError(FD_ERR_UNSUPPORTED, "the query of an E4M3 cache is bf16")
+    for sc, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if sc is not None and (sc.dtype != torch.float32 or tuple(sc.shape) != (Hkv,)):
+            raise FdError(FD_ERR_INVALID_ARG, f"{name} must be float32 [Hkv]")
+    if lens is not None and (lens.dtype != torch.int32 or lens.shape != (B,)):
+        raise FdError(FD_ERR_INVALID_ARG, "lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise FdError(FD_ERR_INVALID_ARG, "out must be [B, Hq, D]")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = decode_workspace_size(B, Hq, Hkv, D, Lmax, FD_FP8_E4M3, n_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fd_decode_attn_fp8(_dev_ptr(q, "q"), _fp8_codes(k, "k"), _fp8_codes(v, "v"),
+                                  _opt_ptr(k_scale, "k_scale"), _opt_ptr(v_scale, "v_scale"), _opt_ptr(lens, "lens"),
+                                  B, Hq, Hkv, D, Lmax, int(n_splits), _dev_ptr(out, "out"), _dtype_code(out),
+                                  _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

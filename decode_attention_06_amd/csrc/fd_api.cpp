@@ -48,7 +48,8 @@ fd_status check_heads(int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype) {
     if (Hq <= 0 || Hkv <= 0) return fail(FD_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
     if (Hq % Hkv != 0) return fail(FD_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (D != 64 && D != 128) return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", D);
-    if (dtype != FD_F32 && dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (dtype != FD_F32 && dtype != FD_BF16 && dtype != FD_FP8_E4M3)
+        return fail(FD_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
     return FD_OK;
 }
 
@@ -105,7 +106,7 @@ struct Path {
 };
 
 Path choose_path(int32_t dtype, int32_t D, int G) {
-    const bool mfma_ok = dtype == FD_BF16 && D == 128;
+    const bool mfma_ok = (dtype == FD_BF16 || dtype == FD_FP8_E4M3) && D == 128;
     bool mfma = mfma_ok && G >= kMfmaMinGroup;
     if (mfma_ok) {
         if (const char* env = std::getenv("FD_PARTIAL_KERNEL")) {
@@ -115,14 +116,15 @@ Path choose_path(int32_t dtype, int32_t D, int G) {
     }
     Path path;
     path.mfma = mfma;
-    path.rows_per_block = mfma ? fd::mfma_rows_per_block(G) : fd::valu_rows_per_block(G);
+    path.rows_per_block = mfma ? fd::mfma_rows_per_block(G) : fd::valu_rows_per_block(G, dtype == FD_FP8_E4M3);
     path.row_blocks = (G + path.rows_per_block - 1) / path.rows_per_block;
     return path;
 }
 
 hipError_t launch_partial(const fd::PartialParams& p, const Path& path, int32_t dtype, int32_t D,
                           hipStream_t s) {
-    return path.mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, dtype, D, path.rows_per_block, s);
+    return path.mfma ? fd::launch_partial_mfma(p, dtype == FD_FP8_E4M3, s)
+                     : fd::launch_partial_valu(p, dtype, D, path.rows_per_block, s);
 }
 
 constexpr int64_t kMinContextPiece = 256;   // shortest context piece planned
@@ -180,7 +182,8 @@ int32_t fd_version(void) { return 100; }
 int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int64_t max_len, int32_t dtype, int32_t n_cu) {
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_len <= 0 ||
-        n_cu <= 0 || num_q_heads % num_kv_heads != 0 || (dtype != FD_F32 && dtype != FD_BF16))
+        n_cu <= 0 || num_q_heads % num_kv_heads != 0 ||
+        (dtype != FD_F32 && dtype != FD_BF16 && dtype != FD_FP8_E4M3))
         return -1;
     const int G = num_q_heads / num_kv_heads;
     const Path path = choose_path(dtype, head_dim, G);
@@ -310,6 +313,8 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
                          int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype,
                          int32_t n_splits, void* out, int32_t out_dtype, float* lse_out, float scale,
                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype == FD_FP8_E4M3)
+        return fail(FD_ERR_UNSUPPORTED, "an E4M3 cache goes through fd_decode_attn_fp8 (it needs the scales)");
     FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
     FD_TRY(check_ptr(k, 16, "k"));
     FD_TRY(check_ptr(v, 16, "v"));
@@ -319,6 +324,27 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
     p.kv_stride_h = Lmax * D;
     p.kv_stride_b = int64_t(Hkv) * Lmax * D;
     return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
+                      workspace, workspace_bytes, stream);
+}
+
+fd_status fd_decode_attn_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                             const float* v_scale, const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t D, int64_t Lmax, int32_t n_splits, void* out, int32_t out_dtype,
+                             float* lse_out, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, FD_FP8_E4M3, n_splits));
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    if (k_scale && !aligned(k_scale, 4)) return fail(FD_ERR_INVALID_ARG, "k_scale is not 4-byte aligned");
+    if (v_scale && !aligned(v_scale, 4)) return fail(FD_ERR_INVALID_ARG, "v_scale is not 4-byte aligned");
+    fd::PartialParams p{};
+    p.k = k;
+    p.v = v;
+    p.kv_stride_h = Lmax * D;
+    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, FD_FP8_E4M3, n_splits, out, out_dtype, lse_out, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -334,6 +360,7 @@ fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v
         return fail(FD_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31 - 1]", (long long)num_pages);
     if (max_pages <= 0) return fail(FD_ERR_INVALID_ARG, "max_pages_per_seq must be positive (got %d)", max_pages);
     const int64_t Lmax = int64_t(max_pages) * page_size;
+    if (dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "paged calls take fp32 or bf16 caches");
     FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
     FD_TRY(check_ptr(k_pages, 16, "k_pages"));
     FD_TRY(check_ptr(v_pages, 16, "v_pages"));
@@ -357,6 +384,7 @@ fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, c
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
                                   int32_t dtype, int32_t n_splits, float* o_part, float* lse_part,
                                   float scale, void* stream) {
+    if (dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "the partial stage takes fp32 or bf16 caches");
     FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
     if (n_splits <= 0) return fail(FD_ERR_INVALID_ARG, "n_splits must be given (> 0) for the partial stage");
     FD_TRY(check_ptr(q, 16, "q"));
@@ -408,6 +436,7 @@ static fd_status check_bifurcated_shapes(int32_t S, int32_t Hq, int32_t Hkv, int
         return fail(FD_ERR_INVALID_ARG, "ctx_len %lld outside [1, 2^30]", (long long)Lc);
     if (Ld <= 0 || Ld > kMaxLen)
         return fail(FD_ERR_INVALID_ARG, "dec_max_len %lld outside [1, 2^30]", (long long)Ld);
+    if (dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "bifurcated calls take fp32 or bf16 inputs");
     return check_heads(Hq, Hkv, D, dtype);
 }
 

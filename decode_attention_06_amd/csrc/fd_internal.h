@@ -43,6 +43,10 @@ struct PartialParams {
     int64_t page_stride;    // elements per page (Hkv * page_size * D)
     int32_t page_shift;     // log2(page_size), page_size >= 16
     int32_t n_pages;
+    // E4M3 cache: per-KV-head scales [Hkv] (cache value = code value *
+    // scale), or nullptr = 1.  The query stays bf16.
+    const float* k_scale;
+    const float* v_scale;
 };
 
 // Context part of a bifurcated call on the matrix cores (bf16, head_dim
@@ -71,9 +75,12 @@ int bif_context_row_tiles(int S, int G);
 hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, hipStream_t stream);
 
 // Query rows handled by one work unit of the vector-ALU partial kernel for a
-// GQA group of G query heads: the largest of 8, 4, 2, 1 that divides G.
-inline int valu_rows_per_block(int G) {
-    return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+// GQA group of G query heads: the largest of 8, 4, 2, 1 that divides G (at
+// most 4 for an E4M3 cache, whose 16-element lane slices double the
+// per-row registers).
+inline int valu_rows_per_block(int G, bool fp8_cache = false) {
+    const int r = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    return (fp8_cache && r > 4) ? 4 : r;
 }
 
 // Rows per work unit of the matrix-core kernel (16 or 32) for a group of G.
@@ -87,8 +94,9 @@ int mfma_waves_per_unit(int units);
 
 // Matrix-core partial kernel: bf16, head_dim 128, any G (row_blocks =
 // ceil(G / mfma_rows_per_block(G))).
-hipError_t launch_partial_mfma(const PartialParams& p, hipStream_t stream);
+hipError_t launch_partial_mfma(const PartialParams& p, bool fp8_cache, hipStream_t stream);
 
+// dtype: 0 fp32, 1 bf16, 2 E4M3 cache with a bf16 query.
 hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, int rows_per_block,
                                hipStream_t stream);
 

@@ -37,6 +37,7 @@ struct Vec16;
 template <>
 struct Vec16<float> {
     static constexpr int N = 4;
+    static constexpr int BYTES = 4;
     __device__ static void unpack(const uint4& r, float* f) {
         f[0] = __uint_as_float(r.x);
         f[1] = __uint_as_float(r.y);
@@ -48,12 +49,44 @@ struct Vec16<float> {
 template <>
 struct Vec16<uint16_t> {  // bf16 bits
     static constexpr int N = 8;
+    static constexpr int BYTES = 2;
     __device__ static void unpack(const uint4& r, float* f) {
         f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
         f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
         f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
         f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
     }
+};
+
+// OCP E4M3 codes (the cache of the fp8 entry point; its query is bf16).
+struct Fp8E4M3 {};
+
+template <>
+struct Vec16<Fp8E4M3> {
+    static constexpr int N = 16;
+    static constexpr int BYTES = 1;
+    __device__ static void unpack(const uint4& r, float* f) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+            f[4 * k + 0] = lo[0];
+            f[4 * k + 1] = lo[1];
+            f[4 * k + 2] = hi[0];
+            f[4 * k + 3] = hi[1];
+        }
+    }
+};
+
+// Storage type of the query for a cache element type.
+template <typename T>
+struct QueryOf {
+    using type = T;
+};
+template <>
+struct QueryOf<Fp8E4M3> {
+    using type = uint16_t;
 };
 
 // Sum over each aligned group of LPR lanes; every lane of the group ends
@@ -84,7 +117,10 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     constexpr int EPL = Vec16<T>::N;     // elements per lane per row
     constexpr int LPR = D / EPL;         // lanes per KV row
     constexpr int RPW = 64 / LPR;        // KV rows per wave-wide load
-    constexpr int U = (GB <= 2) ? 8 : 4; // loads in flight per lane, per K and V
+    // Loads in flight per lane, per K and V and buffer.  An E4M3 load holds
+    // 16 elements, twice a bf16 load: half as many keep the registers (and
+    // the load instructions in flight) the same.
+    constexpr int U = ((GB <= 2) ? 8 : 4) / (EPL == 16 ? 2 : 1);
     constexpr int NW = 4;                // waves per workgroup
     constexpr int WAVE_TOK = RPW * U;
     constexpr int WG_TOK = NW * WAVE_TOK;
@@ -116,25 +152,32 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     const int t0 = (int)min((int64_t)split * chunk, (int64_t)n);
     const int t1 = min(t0 + chunk, n);
 
-    // Query slice of this lane, pre-multiplied by scale*log2(e) so that
-    // exp2 of a score difference is the softmax weight ratio.
+    // Query slice of this lane, pre-multiplied by scale*log2(e) (and the
+    // KV head's K scale for an E4M3 cache) so that exp2 of a score
+    // difference is the softmax weight ratio.
+    using TQ = typename QueryOf<T>::type;
+    const float sl2 = p.scale_log2 * (p.k_scale ? p.k_scale[kvh] : 1.f);
+    const float vsc = p.v_scale ? p.v_scale[kvh] : 1.f;
     float qf[GB][EPL];
 #pragma unroll
     for (int g = 0; g < GB; ++g) {
-        const T* qp = static_cast<const T*>(p.q) + ((int64_t)b * p.Hq + h0 + g) * D + c * EPL;
-        Vec16<T>::unpack(*reinterpret_cast<const uint4*>(qp), qf[g]);
+        const TQ* qp = static_cast<const TQ*>(p.q) + ((int64_t)b * p.Hq + h0 + g) * D + c * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
+        for (int e = 0; e < EPL; e += Vec16<TQ>::N)
+            Vec16<TQ>::unpack(*reinterpret_cast<const uint4*>(qp + e), &qf[g][e]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qf[g][e] *= sl2;
     }
 
     // Rows are addressed per 16-row group: a wave-uniform 64-bit base (the
     // dense slice's row, or the row's page) plus a 32-bit lane offset below
-    // 16 * D * sizeof(T), so each load takes one offset register.  A wave
+    // 16 rows of D elements, so each load takes one offset register.  A wave
     // tile covers NG groups; the rows of load u lie in group u * RPW / 16.
     const char* kpool = static_cast<const char*>(p.k);
     const char* vpool = static_cast<const char*>(p.v);
     const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
-    const uint32_t lane_off = c * EPL * (uint32_t)sizeof(T);
+    constexpr int SZ = Vec16<T>::BYTES;
+    const uint32_t lane_off = c * EPL * (uint32_t)SZ;
     constexpr int NG = WAVE_TOK >= 16 ? WAVE_TOK / 16 : 1;
     static_assert(16 % RPW == 0, "a load's rows must stay inside one 16-row group");
 
@@ -167,17 +210,17 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 #pragma unroll
         for (int h = 0; h < NG; ++h) {
             if constexpr (PAGED) {
-                gb[h] = kv_page_offset<D>(p, gid[h], kvh, gs[h]) * (int64_t)sizeof(T);
+                gb[h] = kv_page_offset<D>(p, gid[h], kvh, gs[h]) * (int64_t)SZ;
             } else {
                 gs[h] = kv_group_start(tb + 16 * h, t1 - 1);
-                gb[h] = (slice + (int64_t)gs[h] * D) * (int64_t)sizeof(T);
+                gb[h] = (slice + (int64_t)gs[h] * D) * (int64_t)SZ;
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int h = (NG > 1) ? (u * RPW) / 16 : 0;
             const int t = min(tb + u * RPW + r, t1 - 1);
-            const uint32_t off = (uint32_t)(t - gs[h]) * (uint32_t)(D * sizeof(T)) + lane_off;
+            const uint32_t off = (uint32_t)(t - gs[h]) * (uint32_t)(D * SZ) + lane_off;
             kr[u] = *reinterpret_cast<const uint4*>(kpool + gb[h] + off);
             vr[u] = *reinterpret_cast<const uint4*>(vpool + gb[h] + off);
         }
@@ -324,7 +367,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
                 A = fmaf(s_acc[w][g][d], a, A);
             }
         }
-        const float o = (L > 0.f) ? A / L : 0.f;
+        const float o = (L > 0.f) ? A / L * vsc : 0.f;
         const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
         const int64_t row = (int64_t)b * p.Hq + h0 + g;
         if (p.direct) {
@@ -581,7 +624,11 @@ hipError_t launch_valu_rows(const PartialParams& p, int rows_per_block, hipStrea
         case 1: hipLaunchKernelGGL((partial_valu_kernel<T, D, 1, PAGED>), grid, block, 0, stream, p); break;
         case 2: hipLaunchKernelGGL((partial_valu_kernel<T, D, 2, PAGED>), grid, block, 0, stream, p); break;
         case 4: hipLaunchKernelGGL((partial_valu_kernel<T, D, 4, PAGED>), grid, block, 0, stream, p); break;
-        case 8: hipLaunchKernelGGL((partial_valu_kernel<T, D, 8, PAGED>), grid, block, 0, stream, p); break;
+        case 8:
+            // An E4M3 cache uses at most 4 rows per unit (valu_rows_per_block).
+            if constexpr (Vec16<T>::N == 16) return hipErrorInvalidValue;
+            else hipLaunchKernelGGL((partial_valu_kernel<T, D, 8, PAGED>), grid, block, 0, stream, p);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -600,6 +647,9 @@ hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, 
     if (dtype == 0) {
         if (head_dim == 64) return launch_valu_layout<float, 64>(p, rows_per_block, stream);
         if (head_dim == 128) return launch_valu_layout<float, 128>(p, rows_per_block, stream);
+    } else if (dtype == 2) {
+        if (head_dim == 64) return launch_valu_layout<Fp8E4M3, 64>(p, rows_per_block, stream);
+        if (head_dim == 128) return launch_valu_layout<Fp8E4M3, 128>(p, rows_per_block, stream);
     } else {
         if (head_dim == 64) return launch_valu_layout<uint16_t, 64>(p, rows_per_block, stream);
         if (head_dim == 128) return launch_valu_layout<uint16_t, 128>(p, rows_per_block, stream);

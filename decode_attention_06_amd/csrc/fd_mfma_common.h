@@ -19,6 +19,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int MF_D = 128;
 constexpr int MF_TILE = 32;   // tokens per wave tile
@@ -26,7 +27,22 @@ constexpr int MF_NW = 4;      // waves per workgroup (split-KV kernel)
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+__device__ __forceinline__ u32x4_t ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Eight OCP E4M3 codes (two dwords, memory order) -> eight bf16 (four
+// dwords), memory order kept (v_cvt_scalef32_pk_bf16_fp8 with scale 1:
+// every E4M3 value is exact in bf16).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    return r;
+}
 
 // Column e of the 8x8 bf16 block r[0..7] (row j = r[j], 8 elements each):
 // {r[0][e], r[1][e], ..., r[7][e]}, packed two per dword.

@@ -1,11 +1,14 @@
-// Split-KV partial work unit on the matrix cores (gfx950, bf16, D = 128),
-// shared by the split-KV kernel and the decode role of the bifurcated
-// kernel.  Internal.  See fd_mfma.hip for the method and the layouts.
+// Split-KV partial work unit on the matrix cores (gfx950, D = 128, bf16
+// or OCP E4M3 cache with a bf16 query), shared by the split-KV kernel and
+// the decode role of the bifurcated kernel.  Internal.  See fd_mfma.hip for
+// the method and the layouts.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fd_device.h"
 #include "fd_internal.h"
@@ -15,32 +18,93 @@
 namespace fd {
 namespace {
 
-// Loads one 32-token tile starting at row tb (tb < t1): K in score
-// A-operand layout, V as this lane's 8x8 block (rows 8g .. 8g+7, columns
-// 8i .. 8i+7).  Every load is issued unconditionally; a row index at or
-// beyond t1 is clamped to t1 - 1, a valid row, whose score is masked to -inf
-// later, so no row past the sequence length is ever read.
-__device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t* vbase, int tb, int t1,
-                                          int ktok0, int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
-    const int last = t1 - 1;
+// Registers of one 32-token tile as loaded.
+//  bf16 cache: K in score A-operand layout (token block blk, k-step s: lane
+//  (g, i) holds token 8*(i/4) + 4*blk + i%4, d = 32s + 8g .. +8) and V as
+//  the lane's 8x8 block (tokens 8g .. 8g+7, d = 8i .. 8i+7).
+//  E4M3 cache: K as the lane's 32 contiguous codes of its token, d = 32g ..
+//  32g+31 (k-step s takes d = 32g + 8s .. +8; the query fragments use the
+//  same assignment, the contraction over d does not depend on it) and V as
+//  the lane's 8x8 block of codes.  Codes become bf16 (exactly) only when the
+//  tile is computed, so the loads stay in flight meanwhile.
+struct Bf16Tile {
+    u32x4_t k[2][4];
+    u32x4_t v[8];
+};
+struct Fp8Tile {
+    u32x4_t k[2][2];
+    u32x2_t v[8];
+};
+
+// Loads one tile starting at row tb (tb < t1).  Every load is issued
+// unconditionally; a row index at or beyond t1 is clamped to t1 - 1, a valid
+// row whose score is masked to -inf later, so no row past the sequence
+// length is ever read.  `kb`, `vb`: element offsets from the pool to row 0
+// of the lane's K and V rows (dense: the (b, kvh) slice; paged: per group).
+__device__ __forceinline__ void load_rows(const uint16_t* kpool, const uint16_t* vpool, int64_t ko, int64_t vo,
+                                          int tb, int last, int ktok0, int g, int i, Bf16Tile& r) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int t = min(tb + ktok0 + 4 * blk, last);
-        const uint16_t* src = kbase + (int64_t)t * MF_D + 8 * g;
+        const uint16_t* src = kpool + ko + (int64_t)t * MF_D + 8 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kr[blk][s] = ld16(src + 32 * s);
+        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16(src + 32 * s);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = min(tb + 8 * g + j, last);
-        vr[j] = ld16(vbase + (int64_t)t * MF_D + 8 * i);
+        r.v[j] = ld16(vpool + vo + (int64_t)t * MF_D + 8 * i);
     }
 }
 
+__device__ __forceinline__ void load_rows(const uint8_t* kpool, const uint8_t* vpool, int64_t ko, int64_t vo,
+                                          int tb, int last, int ktok0, int g, int i, Fp8Tile& r) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int t = min(tb + ktok0 + 4 * blk, last);
+        const uint8_t* src = kpool + ko + (int64_t)t * MF_D + 32 * g;
+        r.k[blk][0] = ld16(src);
+        r.k[blk][1] = ld16(src + 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = min(tb + 8 * g + j, last);
+        r.v[j] = ld8(vpool + vo + (int64_t)t * MF_D + 8 * i);
+    }
+}
+
+// Computes one loaded tile (see compute_tile).
+template <int NRB>
+__device__ __forceinline__ void compute_loaded(const Bf16Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
+                                               int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
+                                               f32x4_t (&acc)[NRB][8]) {
+    compute_tile<NRB>(r.k, r.v, qb, tb, t1, g, sl2, m, lacc, acc);
+}
+
+template <int NRB>
+__device__ __forceinline__ void compute_loaded(const Fp8Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
+                                               int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
+                                               f32x4_t (&acc)[NRB][8]) {
+    u32x4_t kr[2][4], vr[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4_t& w = r.k[blk][s >> 1];
+            const int d0 = (s & 1) * 2;
+            kr[blk][s] = fp8x8_to_bf16(w[d0], w[d0 + 1]);
+        }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
+    compute_tile<NRB>(kr, vr, qb, tb, t1, g, sl2, m, lacc, acc);
+}
+
 // Paged tiles.  A tile (16-row aligned) covers two 16-row groups, each
-// inside one page: PagedTile holds their first rows and element offsets
-// (wave-uniform; the page ids come from scalar loads, looked up one tile
-// ahead so that their latency hides behind the current tile's work).
+// inside one page: PagedTile holds their first rows and page ids (wave-
+// uniform; the ids come from scalar loads, looked up one tile ahead so that
+// their latency hides behind the current tile's work).  A lane's K rows lie
+// in group i / 8 and its V rows in group g / 2; rows at or beyond t1 clamp
+// to t1 - 1, and kv_group_start gives the group that then holds them.
 struct PagedTile {
     int s0, s1;       // first rows of the two groups
     int id0, id1;     // their page ids (table entries)
@@ -55,32 +119,6 @@ __device__ __forceinline__ PagedTile paged_tile(const PartialParams& p, int b, i
     return r;
 }
 
-// Paged form of load_tile.  A lane's K rows lie in group i / 8 and its V
-// rows in group g / 2; rows at or beyond t1 clamp to t1 - 1 as above, and
-// kv_group_start gave the group that then holds them.
-__device__ __forceinline__ void load_tile_paged(const PartialParams& p, int kvh, const uint16_t* kpool,
-                                                const uint16_t* vpool, const PagedTile& r, int tb, int t1,
-                                                int ktok0, int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
-    const int last = t1 - 1;
-    const int64_t o0 = kv_page_offset<MF_D>(p, r.id0, kvh, r.s0) - (int64_t)r.s0 * MF_D;
-    const int64_t o1 = kv_page_offset<MF_D>(p, r.id1, kvh, r.s1) - (int64_t)r.s1 * MF_D;
-    const bool khi = i >= 8, vhi = g >= 2;
-    const int64_t ko = (khi ? o1 : o0) + 8 * g;
-    const int64_t vo = (vhi ? o1 : o0) + 8 * i;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const int t = min(tb + ktok0 + 4 * blk, last);
-        const uint16_t* src = kpool + ko + (int64_t)t * MF_D;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kr[blk][s] = ld16(src + 32 * s);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int t = min(tb + 8 * g + j, last);
-        vr[j] = ld16(vpool + vo + (int64_t)t * MF_D);
-    }
-}
-
 // NRB blocks of 16 query rows per work unit share every K/V load; NW waves
 // per workgroup take interleaved 32-token tiles of the unit's piece.
 template <int NRB, int NW>
@@ -91,8 +129,10 @@ struct PartialLds {
     float l[NW][ROWS];
 };
 
-template <int NRB, int NW, bool PAGED = false>
+template <int NRB, int NW, bool PAGED = false, bool KV8 = false>
 __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bid, PartialLds<NRB, NW>& sh) {
+    using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+    using Tile = typename std::conditional<KV8, Fp8Tile, Bf16Tile>::type;
     constexpr int D = MF_D, ROWS = 16 * NRB;
     auto& s_acc = sh.acc;
     auto& s_m = sh.m;
@@ -121,6 +161,8 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     const int t1 = min(t0 + chunk, n);
 
     // Q^T fragments (B operand of the score product); rows >= nr are zero.
+    // k-step s of lane group g covers d = 32s + 8g .. +8 (bf16 cache) or
+    // d = 32g + 8s .. +8 (E4M3 cache), as the K fragments do.
     bf16x8_t qb[NRB][4];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -128,18 +170,21 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             u32x4_t v = {0u, 0u, 0u, 0u};
-            if (row < nr)
-                v = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h0 + row) * D + 32 * s + 8 * g);
+            const int d0 = KV8 ? 32 * g + 8 * s : 32 * s + 8 * g;
+            if (row < nr) v = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h0 + row) * D + d0);
             qb[r][s] = as_bf16x8(v);
         }
     }
 
+    const Elem* kpool = static_cast<const Elem*>(p.k);
+    const Elem* vpool = static_cast<const Elem*>(p.v);
     const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
-    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + slice;
-    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + slice;
     // Token offsets inside a tile for this lane's K rows (one per token block).
     const int ktok0 = 8 * (i >> 2) + (i & 3);
-    const float sl2 = p.scale_log2;
+    // Per-KV-head cache scales (E4M3): K's folds into the score scale, V's
+    // into the piece's output.
+    const float sl2 = p.scale_log2 * (p.k_scale ? p.k_scale[kvh] : 1.f);
+    const float vsc = p.v_scale ? p.v_scale[kvh] : 1.f;
 
     f32x4_t acc[NRB][8], lacc[NRB];
     float m[NRB];
@@ -157,28 +202,32 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // every path leaves the same number of loads outstanding and the wait
     // before each tile covers only that tile's own loads.
     constexpr int STEP = NW * MF_TILE;
-    u32x4_t ka[2][4], va[8], kb2[2][4], vb2[8];
-    // Paged: `ahead` holds the page offsets of the next tile to load.
+    Tile ta, tn;
+    // Paged: `ahead` holds the page ids of the next tile to load.
     PagedTile ahead{};
-    auto load = [&](int at, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
+    auto load = [&](int at, Tile& r) {
         if constexpr (PAGED) {
-            load_tile_paged(p, kvh, kbase, vbase, ahead, at, t1, ktok0, g, i, kr, vr);
+            // Offsets to row 0 of each group's page (row t of the group
+            // then sits at offset + t * D).
+            const int64_t o0 = kv_page_offset<MF_D>(p, ahead.id0, kvh, ahead.s0) - (int64_t)ahead.s0 * MF_D;
+            const int64_t o1 = kv_page_offset<MF_D>(p, ahead.id1, kvh, ahead.s1) - (int64_t)ahead.s1 * MF_D;
+            load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, at, t1 - 1, ktok0, g, i, r);
             ahead = paged_tile(p, b, at + STEP, t1 - 1);
         } else {
-            load_tile(kbase, vbase, at, t1, ktok0, g, i, kr, vr);
+            load_rows(kpool, vpool, slice, slice, at, t1 - 1, ktok0, g, i, r);
         }
     };
     int tb = t0 + wave * MF_TILE;
     if (tb < t1) {
         if constexpr (PAGED) ahead = paged_tile(p, b, tb, t1 - 1);
-        load(tb, ka, va);
+        load(tb, ta);
         while (true) {
-            load(tb + STEP, kb2, vb2);
-            compute_tile<NRB>(ka, va, qb, tb, t1, g, sl2, m, lacc, acc);
+            load(tb + STEP, tn);
+            compute_loaded<NRB>(ta, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;
-            load(tb + STEP, ka, va);
-            compute_tile<NRB>(kb2, vb2, qb, tb, t1, g, sl2, m, lacc, acc);
+            load(tb + STEP, ta);
+            compute_loaded<NRB>(tn, qb, tb, t1, g, sl2, m, lacc, acc);
             tb += STEP;
             if (tb >= t1) break;
         }
@@ -215,7 +264,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
                 A = fmaf(s_acc[w][row][d], a, A);
             }
         }
-        const float o = (L > 0.f) ? A / L : 0.f;
+        const float o = (L > 0.f) ? A / L * vsc : 0.f;
         const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
         const int64_t orow = (int64_t)b * p.Hq + h0 + row;
         if (p.direct) {

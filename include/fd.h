@@ -39,7 +39,8 @@
  *        out  [B, Hq, D]
  *    q, k, v and out must be 16-byte aligned; lens, lse buffers 4-byte.
  *  - Query head h reads KV head h / (Hq / Hkv) (contiguous groups).
- *  - Supported: q/k/v dtype FD_F32 or FD_BF16 (all three the same), out
+ *  - Supported: q/k/v dtype FD_F32 or FD_BF16 (all three the same), or,
+ *    for fd_decode_attn_fp8 only, FD_FP8_E4M3 (E4M3 cache, bf16 query); out
  *    dtype FD_F32 or FD_BF16 (bf16 is rounded to nearest even), head_dim
  *    64 or 128, Hq a multiple of Hkv.  Anything else returns
  *    FD_ERR_UNSUPPORTED; there is no silent fallback.
@@ -73,7 +74,11 @@ typedef enum fd_status {
 
 typedef enum fd_dtype {
     FD_F32 = 0,
-    FD_BF16 = 1
+    FD_BF16 = 1,
+    /* K/V cache of OCP 8-bit floating point E4M3 codes (1 byte each) with a
+     * bf16 query; for fd_decode_attn_fp8, fd_plan_splits and
+     * fd_decode_attn_workspace_size. */
+    FD_FP8_E4M3 = 2
 } fd_dtype;
 
 /* Largest split count accepted (per sequence for decode; context plus
@@ -150,6 +155,27 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
                          int32_t head_dim, int64_t max_len, int32_t dtype,
                          int32_t n_splits, void* out, int32_t out_dtype, float* lse_out,
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fd_decode_attn_fp8 - fd_decode_attn over a KV cache of 8-bit floating
+ * point codes ([MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", quantisation
+ * paragraph: fewer bits per stored value, fewer bytes over the memory bus).
+ * Codes are OCP E4M3 ("fn": bias 7, no infinities, 0x7F/0xFF NaN, largest
+ * finite 448); cache value = code value * the KV head's scale.  Every code
+ * is exact in bf16; products run on bf16 with fp32 accumulation.
+ *
+ *   q                bf16 [B, Hq, D]
+ *   k, v             uint8 codes [B, Hkv, Lmax, D]
+ *   k_scale, v_scale device fp32 [Hkv], positive and finite, or NULL = 1
+ *   everything else  as in fd_decode_attn; the workspace size is
+ *                    fd_decode_attn_workspace_size(..., FD_FP8_E4M3, ...)
+ */
+fd_status fd_decode_attn_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                             const float* v_scale, const int32_t* lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int64_t max_len, int32_t n_splits, void* out, int32_t out_dtype,
+                             float* lse_out, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * fd_decode_attn_paged - fd_decode_attn over a paged KV cache ([MW] "ಮೆಮೊರಿ

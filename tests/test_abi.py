@@ -165,6 +165,47 @@ def test_paged_rejects_before_any_hip_call(lib, kw, status):
     assert lib.fd_last_error_message().decode()
 
 
+def _fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, lens=None, B=2, Hq=8, Hkv=2, D=128, L=512, n_splits=4,
+             out=FAKE, out_dtype=fd.FD_BF16, lse=None, scale=0.0, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.fd_decode_attn_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["lens"], a["B"], a["Hq"], a["Hkv"],
+                                  a["D"], a["L"], a["n_splits"], a["out"], a["out_dtype"], a["lse"], a["scale"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), fd.FD_ERR_INVALID_ARG),
+    (dict(v=MISALIGNED), fd.FD_ERR_INVALID_ARG),
+    (dict(ks=0x10002), fd.FD_ERR_INVALID_ARG),
+    (dict(vs=0x10001), fd.FD_ERR_INVALID_ARG),
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), fd.FD_ERR_UNSUPPORTED),
+    (dict(L=0), fd.FD_ERR_INVALID_ARG),
+    (dict(out_dtype=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(ws=None), fd.FD_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fd.FD_ERR_WORKSPACE),
+])
+def test_fp8_rejects_before_any_hip_call(lib, kw, status):
+    st = _fp8(lib, **kw)
+    assert st == status, (st, fd.load().fd_last_error_message())
+    assert lib.fd_last_error_message().decode()
+
+
+def test_fp8_dtype_only_through_its_entry_point(lib):
+    assert _decode(lib, dtype=fd.FD_FP8_E4M3, D=128, Hq=8, Hkv=2) == fd.FD_ERR_UNSUPPORTED
+    assert _paged(lib, dtype=fd.FD_FP8_E4M3) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_decode_attn_partials(FAKE, FAKE, FAKE, None, 1, 8, 2, 128, 512, fd.FD_FP8_E4M3, 4, FAKE, FAKE,
+                                       0.0, None) == fd.FD_ERR_UNSUPPORTED
+    # planner and workspace size accept it (same partial layout as bf16)
+    assert fd.plan_splits(1, 16, 2, 128, 65536, fd.FD_FP8_E4M3, 256) == fd.plan_splits(1, 16, 2, 128, 65536,
+                                                                                       fd.FD_BF16, 256)
+    n8, n16 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.fd_decode_attn_workspace_size(1, 16, 2, 128, 4096, fd.FD_FP8_E4M3, 8, ctypes.byref(n8)) == fd.FD_OK
+    assert lib.fd_decode_attn_workspace_size(1, 16, 2, 128, 4096, fd.FD_BF16, 8, ctypes.byref(n16)) == fd.FD_OK
+    assert n8.value == n16.value > 0
+
+
 def test_bifurcated_rejects_bad_arguments(lib):
     def call(**kw):
         a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=FAKE, vd=FAKE, dl=None, S=4, Hq=8, Hkv=2, D=128, Lc=64, Ld=8,
@@ -182,6 +223,7 @@ def test_bifurcated_rejects_bad_arguments(lib):
     assert call(D=80) == fd.FD_ERR_UNSUPPORTED
     assert call(ws=None) == fd.FD_ERR_WORKSPACE
     assert call(dl=0x10003) == fd.FD_ERR_INVALID_ARG
+    assert call(dtype=fd.FD_FP8_E4M3) == fd.FD_ERR_UNSUPPORTED
 
 
 def test_combine_rejects_bad_arguments(lib):

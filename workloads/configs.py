@@ -8,7 +8,8 @@ from dataclasses import dataclass
 
 __all__ = ["DecodeWorkload", "BifurcatedWorkload", "TINY", "CODELLAMA34B_SHARE",
            "MHA_SWEEP", "BIFURCATED_MQA", "BIFURCATED_GQA", "CODELLAMA34B_SHARE_PAGED",
-           "MHA_B16_L65536_PAGED", "ALL_DECODE", "ALL_BIFURCATED", "ALL_PAGED"]
+           "MHA_B16_L65536_PAGED", "CODELLAMA34B_SHARE_FP8", "MHA_B16_L65536_FP8", "ALL_DECODE",
+           "ALL_BIFURCATED", "ALL_PAGED", "ALL_FP8"]
 
 
 @dataclass(frozen=True)
@@ -19,7 +20,7 @@ class DecodeWorkload:
     kv_heads: int
     head_dim: int
     max_len: int
-    dtype: str                 # 'bf16' or 'fp32' (q, K, V storage)
+    dtype: str                 # 'bf16' or 'fp32' (q, K, V storage), or 'fp8' (E4M3 K/V codes, bf16 q)
     ragged: bool               # lens uniform in [max_len/2, max_len] when True
     n_splits: int              # <= 0: split count chosen by the planner
     seed: int
@@ -27,7 +28,7 @@ class DecodeWorkload:
     page_size: int = 0         # > 0: paged cache of pages this many rows long
 
     def kv_bytes_allocated(self):
-        sz = 2 if self.dtype == "bf16" else 4
+        sz = {"bf16": 2, "fp32": 4, "fp8": 1}[self.dtype]
         return 2 * self.batch * self.kv_heads * self.max_len * self.head_dim * sz
 
 
@@ -81,6 +82,14 @@ CODELLAMA34B_SHARE_PAGED = DecodeWorkload("codellama34b_share_paged16_b1_hq16_hk
 MHA_B16_L65536_PAGED = DecodeWorkload("mha_paged16_b16_h32_d128_l65536_bf16", 16, 32, 32, 128, 65536,
                                       "bf16", True, 0, 7, 1e-2, page_size=16)
 
+# E4M3 (fp8) cache forms of the 64K workloads: K and V stored as one-byte
+# codes with per-KV-head scales, the query bf16.
+CODELLAMA34B_SHARE_FP8 = DecodeWorkload("codellama34b_share_fp8kv_b1_hq16_hkv2_d128_l65536",
+                                        1, 16, 2, 128, 65536, "fp8", False, 0, 8, 1e-2)
+MHA_B16_L65536_FP8 = DecodeWorkload("mha_fp8kv_b16_h32_d128_l65536", 16, 32, 32, 128, 65536, "fp8", True, 0,
+                                    9, 1e-2)
+
 ALL_DECODE = (TINY, CODELLAMA34B_SHARE) + MHA_SWEEP
 ALL_PAGED = (CODELLAMA34B_SHARE_PAGED, MHA_B16_L65536_PAGED)
+ALL_FP8 = (CODELLAMA34B_SHARE_FP8, MHA_B16_L65536_FP8)
 ALL_BIFURCATED = (BIFURCATED_MQA, BIFURCATED_GQA)

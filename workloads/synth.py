@@ -22,6 +22,10 @@ __all__ = [
     "device_lengths",
     "paginate",
     "shuffled_block_table",
+    "head_scales",
+    "to_e4m3",
+    "fp8_case",
+    "device_fp8",
 ]
 
 
@@ -168,3 +172,55 @@ def paginate(k, v, lens, page_size, seed):
             kp[page, :, :r1 - r0] = k[b, :, r0:r1]
             vp[page, :, :r1 - r0] = v[b, :, r0:r1]
     return kp, vp, table
+
+
+def head_scales(kv_heads, seed):
+    """Per-KV-head cache scales for an E4M3 cache of N(0, 1) data: about
+    5 / 448 (a 5-sigma value lands near the largest code), varied per head
+    by up to +-25% so that a scale applied to the wrong head shows."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (5.0 / 448.0 * g.uniform(0.75, 1.25, size=kv_heads)).astype(np.float32)
+
+
+def to_e4m3(x, scales):
+    """Codes of x / scale (scale per KV head, axis 1 of x), rounded to the
+    nearest E4M3 value (ties to even) after clamping to +-448, via torch's
+    float8_e4m3fn conversion on the host.  Returns uint8 codes."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    sc = torch.from_numpy(np.asarray(scales, dtype=np.float32)).view(1, -1, *([1] * (t.dim() - 2)))
+    y = (t / sc).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_case(B, Hq, Hkv, D, Lmax, seed, lens=None, pad_nan=True):
+    """Host inputs for one E4M3-cache call: q bf16-rounded N(0,1); K, V drawn
+    N(0,1) and stored as E4M3 codes with per-head scales.  Rows past lens[b]
+    hold the NaN code 0x7F when pad_nan.  Returns dict(q, k_bits, v_bits
+    [B, Hkv, Lmax, D] uint8, k_scale, v_scale [Hkv] float32, lens int32)."""
+    q = host_normal((B, Hq, D), seed, "bf16")
+    k = host_normal((B, Hkv, Lmax, D), seed + 1, "fp32")
+    v = host_normal((B, Hkv, Lmax, D), seed + 2, "fp32")
+    ks, vs = head_scales(Hkv, seed + 3), head_scales(Hkv, seed + 4)
+    kb, vb = to_e4m3(k, ks), to_e4m3(v, vs)
+    if lens is None:
+        lens = np.full(B, Lmax, dtype=np.int64)
+    elif isinstance(lens, tuple):
+        lens = host_lengths(B, lens[0], lens[1], seed + 7)
+    lens = np.asarray(lens, dtype=np.int64)
+    if pad_nan:
+        for b in range(B):
+            kb[b, :, lens[b]:, :] = 0x7F
+            vb[b, :, lens[b]:, :] = 0x7F
+    return {"q": q, "k_bits": kb, "v_bits": vb, "k_scale": ks, "v_scale": vs, "lens": lens.astype(np.int32)}
+
+
+def device_fp8(shape, seed, scales, device):
+    """E4M3 codes (uint8) of N(0,1) draws made on the device, divided by the
+    per-KV-head scales (axis 1) and clamped to +-448 before rounding."""
+    import torch
+
+    x = device_normal(shape, seed, "fp32", device)
+    sc = torch.as_tensor(np.asarray(scales, dtype=np.float32), device=device).view(1, -1, *([1] * (len(shape) - 2)))
+    return (x / sc).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
