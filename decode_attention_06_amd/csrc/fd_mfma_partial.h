@@ -121,10 +121,18 @@ __device__ __forceinline__ PagedTile paged_tile(const PartialParams& p, int b, i
 
 // NRB blocks of 16 query rows per work unit share every K/V load; NW waves
 // per workgroup take interleaved 32-token tiles of the unit's piece.
+// Accumulator element (row, d = 8 (4g + ii) + e) of a wave sits at word
+// row * MF_ACC_STRIDE + acc_col(g, ii, e): with a row stride of 132 words and
+// the lane group g in the low bits of the column, the 64 lanes of one store
+// (rows i = 0..15, groups g = 0..3, fixed ii and e) hit 64 distinct banks,
+// and reads along d conflict at most 2-way.
+constexpr int MF_ACC_STRIDE = MF_D + 4;
+__device__ __forceinline__ int acc_col(int g, int ii, int e) { return 4 * (8 * ii + e) + g; }
+
 template <int NRB, int NW>
 struct PartialLds {
     static constexpr int ROWS = 16 * NRB;
-    float acc[NW][ROWS][MF_D];
+    float acc[NW][ROWS][MF_ACC_STRIDE];
     float m[NW][ROWS];
     float l[NW][ROWS];
 };
@@ -241,7 +249,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
 #pragma unroll
             for (int e = 0; e < 8; ++e)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) s_acc[wave][row][8 * (4 * g + ii) + e] = acc[r][e][ii];
+                for (int ii = 0; ii < 4; ++ii) s_acc[wave][row][acc_col(g, ii, e)] = acc[r][e][ii];
             if (g == 0) {
                 s_m[wave][row] = m[r];
                 s_l[wave][row] = lacc[r][0];
@@ -252,6 +260,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
 
     for (int x = tid; x < nr * D; x += NW * 64) {
         const int row = x / D, d = x % D;
+        const int col = acc_col(d >> 5, (d >> 3) & 3, d & 7);
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][row]);
@@ -261,7 +270,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
             for (int w = 0; w < NW; ++w) {
                 const float a = fast_exp2(s_m[w][row] - M);
                 L = fmaf(s_l[w][row], a, L);
-                A = fmaf(s_acc[w][row][d], a, A);
+                A = fmaf(s_acc[w][row][col], a, A);
             }
         }
         const float o = (L > 0.f) ? A / L * vsc : 0.f;
