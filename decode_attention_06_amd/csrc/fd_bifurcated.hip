@@ -53,11 +53,13 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ sw
 // writes row 8w + 4k + L/16 at chunk position L%16, so it fetches chunk
 // (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1
 // (c1 > t0 is not required: a tile past the end re-reads row c1 - 1).
-// Four vector-memory instructions per wave.
-// Address registers of one wave's loads for a tile (2 per KiB per operand;
-// 4 waves use all four, 8 waves the first two).
+// Addresses are a wave-uniform base (row min(t0, c1 - 1)) plus a 32-bit
+// lane offset below 8 KiB, shared by K and V.  Four vector-memory
+// instructions per wave.
+// Offset registers of one wave's loads for a tile (one per KiB per
+// operand: 4 waves use both, 8 waves the first).
 struct TileAddrs {
-    const uint16_t* p[4];
+    uint32_t off[2];
 };
 
 template <int NW>
@@ -65,6 +67,9 @@ __device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uin
                                                     int wave, int lane, char* kst, char* vst) {
     typedef __attribute__((address_space(3))) void* lds_ptr;
     constexpr int IPW = 8 / NW;             // 1 KiB loads per wave per operand
+    const int tbase = min(t0, c1 - 1);
+    const uint16_t* kt = kbase + (int64_t)tbase * MF_D;
+    const uint16_t* vt = vbase + (int64_t)tbase * MF_D;
     TileAddrs a;
 #pragma unroll
     for (int k = 0; k < IPW; ++k) {
@@ -72,24 +77,46 @@ __device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uin
         const int chunk = (lane & 15) ^ swz(row);
         const int t = min(t0 + row, c1 - 1);
         const int base = 1024 * (IPW * wave + k);
-        a.p[2 * k] = kbase + (int64_t)t * MF_D + 8 * chunk;
-        a.p[2 * k + 1] = vbase + (int64_t)t * MF_D + 8 * chunk;
-        __builtin_amdgcn_global_load_lds(a.p[2 * k], (lds_ptr)(kst + base), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.p[2 * k + 1], (lds_ptr)(vst + base), 16, 0, 0);
+        a.off[k] = (uint32_t)((t - tbase) * MF_D + 8 * chunk);
+        __builtin_amdgcn_global_load_lds(kt + a.off[k], (lds_ptr)(kst + base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + a.off[k], (lds_ptr)(vst + base), 16, 0, 0);
     }
     return a;
 }
 
-// Keeps the address registers of the last issued tile alive up to this
+// Keeps the offset registers of the last issued tile alive up to this
 // point (no instruction is emitted), so the registers of the LDS reads that
 // follow the issue are never the in-flight loads' address registers and the
 // compiler needs no wait for them.
 template <int NW>
 __device__ __forceinline__ void keep_addrs(const TileAddrs& a) {
     if constexpr (NW == 4)
-        asm volatile("" ::"v"(a.p[0]), "v"(a.p[1]), "v"(a.p[2]), "v"(a.p[3]));
+        asm volatile("" ::"v"(a.off[0]), "v"(a.off[1]));
     else
-        asm volatile("" ::"v"(a.p[0]), "v"(a.p[1]));
+        asm volatile("" ::"v"(a.off[0]));
+}
+
+// V^T operand of output block e (d = 16e .. 16e+15) for lane (g, i): the
+// eight values V[8g + j][16e + i], j = 0..7, from two transposing LDS reads
+// (ds_read_b64_tr_b16: within a 16-lane group, lane 4a + c receives element
+// c of the 64-bit rows addressed by lanes a, a+4, a+8, a+12).  For read h,
+// lane i of group g addresses token 8g + 4h + i/4, columns 16e + 4 (i%4) ..
+// +3, so lane i gets tokens 8g + 4h .. +3 of column 16e + i.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
+
+__device__ __forceinline__ u32x4_t v_operand(const char* __restrict__ rv, int e, int g, int i) {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int t = 8 * g + 4 * h + (i >> 2);
+        const int chunk = 2 * e + ((i & 3) >> 1);
+        const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(rv + lds_off(t, chunk) + 8 * (i & 1)));
+        const u32x2_t w = __builtin_bit_cast(u32x2_t, x);
+        r[2 * h] = w[0];
+        r[2 * h + 1] = w[1];
+    }
+    return r;
 }
 
 // One ring step: issue the loads of a later tile into stage (wk, wv) and
@@ -100,7 +127,7 @@ template <int NW>
 __device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint16_t* vbase, int t_issue, int c1,
                                                    int wave, int lane, char* __restrict__ wk, char* __restrict__ wv,
                                                    const char* __restrict__ rk, const char* __restrict__ rv, int ktok0,
-                                                   int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vr)[8]) {
+                                                   int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vt)[8]) {
     const TileAddrs a = issue_tile<NW>(kbase, vbase, t_issue, c1, wave, lane, wk, wv);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -109,8 +136,24 @@ __device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint
         for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4_t*>(rk + lds_off(tt, 4 * s + g));
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const u32x4_t*>(rv + lds_off(8 * g + j, i));
+    for (int e = 0; e < 8; ++e) vt[e] = v_operand(rv, e, g, i);
     return a;
+}
+
+// One tile of the context part: scores, softmax step, then O^T += V^T P^T
+// with the transposed V operands (output row m of block e is d = 16e + m).
+__device__ __forceinline__ void context_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vt)[8],
+                                             const bf16x8_t (&qb)[2][4], int tb, int t1, int g, float sl2,
+                                             float (&m)[2], f32x4_t (&lacc)[2], f32x4_t (&acc)[2][8]) {
+    f32x4_t sc[2][2];
+    tile_scores<2>(kr, qb, sc);
+    bf16x8_t pb[2];
+    tile_softmax<2>(sc, tb, t1, g, sl2, m, lacc, acc, pb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            acc[r][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[e]), pb[r], acc[r][e], 0, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and
@@ -209,26 +252,26 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
         // The query fragments are in registers before the ring starts, so the
         // waits below count tile loads only.
         wait_vm<0>();
-        u32x4_t kr[2][4], vr[8];
+        u32x4_t kr[2][4], vt[8];
 #pragma unroll
         for (int t = 0; t < CTX_STAGES - 1; ++t)
             issue_tile<NW>(kbase, vbase, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
         wait_vm<TWO_TILES>();
         ring_barrier();
         const TileAddrs a0 = ring_step<NW>(kbase, vbase, c0 + (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
-                                       ks[CTX_STAGES - 1], vs[CTX_STAGES - 1], ks[0], vs[0], ktok0, g, i, kr, vr);
+                                       ks[CTX_STAGES - 1], vs[CTX_STAGES - 1], ks[0], vs[0], ktok0, g, i, kr, vt);
         keep_addrs<NW>(a0);
         for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
 #pragma unroll
             for (int st = 0; st < CTX_STAGES; ++st) {
                 const int t = t4 + st;
-                compute_tile<2>(kr, vr, qb, c0 + t * CTX_TILE, c1, g, sl2, m, lacc, acc);
+                context_tile(kr, vt, qb, c0 + t * CTX_TILE, c1, g, sl2, m, lacc, acc);
                 if (t + 1 >= n_tiles) break;
                 wait_vm<TWO_TILES>();
                 ring_barrier();
                 const TileAddrs an = ring_step<NW>(kbase, vbase, c0 + (t + CTX_STAGES) * CTX_TILE, c1, wave, lane,
                                                ks[st], vs[st], ks[(st + 1) % CTX_STAGES], vs[(st + 1) % CTX_STAGES],
-                                               ktok0, g, i, kr, vr);
+                                               ktok0, g, i, kr, vt);
                 keep_addrs<NW>(an);
             }
         }
@@ -247,15 +290,12 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
             const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
             float* dst = p.o_part + slot * MF_D;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                float4 lo, hi;
-                lo.x = acc[r][0][ii] * inv; lo.y = acc[r][1][ii] * inv;
-                lo.z = acc[r][2][ii] * inv; lo.w = acc[r][3][ii] * inv;
-                hi.x = acc[r][4][ii] * inv; hi.y = acc[r][5][ii] * inv;
-                hi.z = acc[r][6][ii] * inv; hi.w = acc[r][7][ii] * inv;
-                // d = 8 * (4g + ii) + e for e = 0..7: eight consecutive floats.
-                *reinterpret_cast<float4*>(dst + 8 * (4 * g + ii)) = lo;
-                *reinterpret_cast<float4*>(dst + 8 * (4 * g + ii) + 4) = hi;
+            for (int e = 0; e < 8; ++e) {
+                // d = 16e + 4g + ii for ii = 0..3: four consecutive floats.
+                float4 o;
+                o.x = acc[r][e][0] * inv; o.y = acc[r][e][1] * inv;
+                o.z = acc[r][e][2] * inv; o.w = acc[r][e][3] * inv;
+                *reinterpret_cast<float4*>(dst + 16 * e + 4 * g) = o;
             }
             if (g == 0) p.lse_part[slot] = (lr > 0.f) ? (m[r] + __log2f(lr)) * kLn2f : -INFINITY;
         }

@@ -66,13 +66,14 @@ __device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t 
     for (int r = 0; r < NRB; ++r) acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], acc[r][E], 0, 0, 0);
 }
 
-// One 32-token tile of the online softmax for NRB blocks of 16 query rows:
-// scores S^T = K Q^T on the matrix cores (K in kr: token block blk, k-step
-// s, lane (g, i) holds token 8*(i/4) + 4*blk + i%4, d = 32s + 8g .. +8),
-// running max per query row (m, log2 domain) and running sum (lacc: every
-// component holds the row's sum), then O^T += V^T P^T (V in vr: lane (g, i)
-// holds tokens 8g .. 8g+7, d = 8i .. 8i+7).  Tokens at or beyond t1 get
-// weight 0.
+// One 32-token tile of the online softmax for NRB blocks of 16 query rows,
+// in three parts: scores S^T = K Q^T on the matrix cores (K in kr: token
+// block blk, k-step s, lane (g, i) holds token 8*(i/4) + 4*blk + i%4,
+// d = 32s + 8g .. +8); the softmax step (running max per query row m, log2
+// domain; running sum lacc, every component holding the row's sum) giving
+// the bf16 weights of this lane's tokens 8g .. 8g+7; and O^T += V^T P^T,
+// where the V^T operand of output block e comes from the caller.  Tokens at
+// or beyond t1 get weight 0.
 // The running maximum m is a reference, not necessarily the exact maximum:
 // it is raised only when a score exceeds it by more than MF_RESCALE_SLACK
 // (log2 units), so weights stay below 2^MF_RESCALE_SLACK and the costly
@@ -81,15 +82,8 @@ __device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t 
 constexpr float MF_RESCALE_SLACK = 8.0f;
 
 template <int NRB>
-__device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
-                                             const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
-                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8]) {
-    const bool full = tb + MF_TILE <= t1;
-    // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
-    // the very weights used in P V, accumulated in fp32 by the matrix core.
-    const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    // All score products first (independent chains for the scheduler).
-    f32x4_t sc[NRB][2];
+__device__ __forceinline__ void tile_scores(const u32x4_t (&kr)[2][4], const bf16x8_t (&qb)[NRB][4],
+                                            f32x4_t (&sc)[NRB][2]) {
 #pragma unroll
     for (int r = 0; r < NRB; ++r)
 #pragma unroll
@@ -99,21 +93,42 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
             for (int s = 0; s < 4; ++s)
                 sc[r][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[r][blk], 0, 0, 0);
         }
-    // Raw scores q.k of this lane's query rows for tokens tb + 8g + j, and
-    // this lane's maximum per row block.
-    float t[NRB][8], mx[NRB];
+}
+
+template <int NRB>
+__device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb, int t1, int g, float sl2,
+                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8],
+                                             bf16x8_t (&pb)[NRB]) {
+    // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
+    // the very weights used in P V, accumulated in fp32 by the matrix core.
+    const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    // Raw scores q.k of this lane's query rows for tokens tb + 8g + j.
+    float t[NRB][8];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[r][j] = sc[r][j >> 2][j & 3];
+    // Only a piece's last tile can hold tokens at or beyond t1.  The empty
+    // asm statements keep this a branch: folded into selects it would run on
+    // every tile.
+    if (tb + MF_TILE > t1) {
+#pragma unroll
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (tb + 8 * g + j >= t1) t[r][j] = -INFINITY;
+                asm volatile("" : "+v"(t[r][j]));
+            }
+    }
+    // This lane's maximum per row block, against the reference (log2
+    // domain, scale * log2(e) folded in; sl2 > 0).
+    float mx[NRB];
     bool raise = false;
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            t[r][j] = sc[r][j >> 2][j & 3];
-            if (!full && tb + 8 * g + j >= t1) t[r][j] = -INFINITY;
-        }
         mx[r] = t[r][0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx[r] = fmaxf(mx[r], t[r][j]);
-        // Reference in the log2 domain (scale * log2(e) folded in; sl2 > 0).
         raise = raise || (mx[r] * sl2 > m[r] + MF_RESCALE_SLACK);
     }
     // Rare path: some score passed its row's reference by more than the
@@ -133,7 +148,6 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
         }
     }
     // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix products.
-    bf16x8_t pb[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         const float ref = (m[r] == -INFINITY) ? 0.f : m[r];
@@ -147,6 +161,19 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
         }
         lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[r], lacc[r], 0, 0, 0);
     }
+}
+
+// Whole tile with V held as the lane's 8x8 block (tokens 8g .. 8g+7,
+// d = 8i .. 8i+7), transposed in registers: output row m of block e is
+// d = 8m + e.
+template <int NRB>
+__device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
+                                             const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
+                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8]) {
+    f32x4_t sc[NRB][2];
+    tile_scores<NRB>(kr, qb, sc);
+    bf16x8_t pb[NRB];
+    tile_softmax<NRB>(sc, tb, t1, g, sl2, m, lacc, acc, pb);
     pv_block<0>(vr, pb, acc);
     pv_block<1>(vr, pb, acc);
     pv_block<2>(vr, pb, acc);
