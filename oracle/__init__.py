@@ -12,5 +12,6 @@ from .fp64 import (  # noqa: F401
     fp8_e4m3_value,
     lse_combine,
     paged_attention,
+    prefill_attention,
     split_partials,
 )

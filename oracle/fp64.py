@@ -56,6 +56,7 @@ __all__ = [
     "paged_attention",
     "fp8_e4m3_value",
     "attention_fp8kv",
+    "prefill_attention",
 ]
 
 
@@ -178,6 +179,50 @@ def paged_attention(q, k_pages, v_pages, block_table, lens=None, scale=None):
             o, l = _attend_rows(q[b, rows], k_pages[page, g, slot], v_pages[page, g, slot], scale)
             out[b, rows] = o
             lse[b, rows] = l
+    return out, lse
+
+
+def prefill_attention(q, k, v, lens=None, scale=None):
+    """Causal many-query (prefill) attention: every position of a sequence
+    attends to the cache rows up to and including its own.
+
+    q     [B, Hq, Lmax, D]   one query per position
+    k, v  [B, Hkv, Lmax, D]
+    lens  [B] integers in [1, Lmax] (None: every sequence is Lmax long)
+    Returns out [B, Hq, Lmax, D] and lse [B, Hq, Lmax]; positions at or
+    beyond lens[b] hold NaN (no query there).
+
+    [FD] "Por qué la decodificación necesita otra planificación": during
+    prefill many query positions are processed in parallel.  [MW] the
+    section on why prompts are fast and generation slow: prefill is
+    matrix-matrix work.  Reading: position p of sequence b sees rows
+    [0, p], i.e. decode attention with lens = p + 1 for each position.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lmax, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape or Lq != Lmax:
+        raise ValueError("shape mismatch between q, k and v")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if lens is None:
+        lens = np.full(B, Lmax, dtype=np.int64)
+    lens = np.asarray(lens, dtype=np.int64)
+    if scale is None:
+        scale = default_scale(D)
+    out = np.full((B, Hq, Lmax, D), np.nan)
+    lse = np.full((B, Hq, Lmax), np.nan)
+    for b in range(B):
+        n = int(lens[b])
+        if not 1 <= n <= Lmax:
+            raise ValueError(f"lens[{b}]={n} outside [1, {Lmax}]")
+        for g in range(Hkv):
+            for p in range(n):
+                rows = slice(g * G, (g + 1) * G)
+                o, l = _attend_rows(q[b, rows, p], k[b, g, :p + 1], v[b, g, :p + 1], scale)
+                out[b, rows, p] = o
+                lse[b, rows, p] = l
     return out, lse
 
 

@@ -17,7 +17,10 @@ AssertionError when the oracle disagrees with:
   page pool by an independently written inverse of the page layout;
 * E4M3 code values against torch's float8_e4m3fn decoder and hand-worked
   landmarks; fp8-cache attention = dense attention on the values that
-  decoder gives, times the per-head scales.
+  decoder gives, times the per-head scales;
+* prefill: position 0 in closed form, every position against 60-digit
+  brute force, and the whole result against torch's causal
+  scaled_dot_product_attention.
 """
 
 import decimal
@@ -373,7 +376,39 @@ def pin_fp8_attention_is_dense_attention(orc):
     _close(lse, ref_lse, 0.0, "fp8 kv lse")
 
 
+def pin_prefill(orc):
+    # position 0 sees only row 0: its value row and its score
+    q, k, v = _rand((1, 4, 9, 8), 170), _rand((1, 2, 9, 8), 171), _rand((1, 2, 9, 8), 172)
+    out, lse = orc.prefill_attention(q, k, v, None, 0.6)
+    _close(out[0, :, 0], np.repeat(v[0, :, 0], 2, axis=0), 0.0, "prefill position 0")
+    _close(lse[0, :, 0], 0.6 * np.einsum("hd,hd->h", q[0, :, 0], np.repeat(k[0, :, 0], 2, axis=0)), 1e-15,
+           "prefill position 0 lse")
+    # 60-digit brute force per position (decode attention with lens = p + 1)
+    B, Hq, Hkv, D, L = 2, 4, 2, 3, 6
+    q, k, v = _rand((B, Hq, L, D), 173, 1.5), _rand((B, Hkv, L, D), 174, 1.5), _rand((B, Hkv, L, D), 175)
+    lens = np.array([6, 4])
+    out, lse = orc.prefill_attention(q, k, v, lens, 0.45)
+    for b in range(B):
+        for p in range(int(lens[b])):
+            ro, rl = _decimal_attention(q[b:b + 1, :, p], k[b:b + 1], v[b:b + 1], np.array([p + 1]), 0.45)
+            _close(out[b, :, p], ro[0], 1e-13, f"prefill decimal b{b} p{p}")
+            _close(lse[b, :, p], rl[0], 1e-13, f"prefill decimal lse b{b} p{p}")
+        assert np.all(np.isnan(out[b, :, int(lens[b]):])), "positions past lens must stay empty"
+    # torch's causal scaled_dot_product_attention (a library routine), KV
+    # repeated per query-head group
+    import torch
+    import torch.nn.functional as F
+
+    B, Hq, Hkv, D, L = 2, 8, 2, 16, 37
+    q, k, v = _rand((B, Hq, L, D), 176), _rand((B, Hkv, L, D), 177), _rand((B, Hkv, L, D), 178)
+    out, _ = orc.prefill_attention(q, k, v)
+    G = Hq // Hkv
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(G, dim=1),
+                                         torch.from_numpy(v).repeat_interleave(G, dim=1), is_causal=True)
+    _close(out, ref.numpy(), 1e-12, "prefill vs torch causal sdpa")
+
+
 ALL_PINS = [pin_golden, pin_decimal_bruteforce, pin_torch_sdpa, pin_closed_forms,
             pin_split_independence, pin_bifurcated_split, pin_gqa_is_repeated_mha,
             pin_row_and_value_invariants, pin_paged_is_dense_attention, pin_fp8_codes,
-            pin_fp8_attention_is_dense_attention]
+            pin_fp8_attention_is_dense_attention, pin_prefill]

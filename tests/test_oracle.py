@@ -25,7 +25,8 @@ def _mutant(**overrides):
         attention=oa.attention, bifurcated_attention=oa.bifurcated_attention,
         split_partials=oa.split_partials, lse_combine=oa.lse_combine,
         default_scale=oa.default_scale, paged_attention=oa.paged_attention,
-        fp8_e4m3_value=oa.fp8_e4m3_value, attention_fp8kv=oa.attention_fp8kv)
+        fp8_e4m3_value=oa.fp8_e4m3_value, attention_fp8kv=oa.attention_fp8kv,
+        prefill_attention=oa.prefill_attention)
     for name, fn in overrides.items():
         setattr(ns, name, fn)
     return ns
@@ -45,7 +46,8 @@ def _with_rows(rows_fn):
         return inner
 
     return _mutant(attention=wrap(oa.attention), bifurcated_attention=wrap(oa.bifurcated_attention),
-                   split_partials=wrap(oa.split_partials), paged_attention=wrap(oa.paged_attention))
+                   split_partials=wrap(oa.split_partials), paged_attention=wrap(oa.paged_attention),
+                   prefill_attention=wrap(oa.prefill_attention))
 
 
 def _rows_no_scale(q, k, v, scale):
@@ -175,6 +177,29 @@ def _fp8_scales_swapped(q, k_bits, v_bits, k_scale=None, v_scale=None, lens=None
     return oa.attention_fp8kv(q, k_bits, v_bits, v_scale, k_scale, lens, scale)
 
 
+def _prefill_window(first, last):
+    """prefill_attention where position p sees rows [first(p), last(p))."""
+    def prefill(q, k, v, lens=None, scale=None):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        B, Hq, L, D = q.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        lens = np.full(B, L) if lens is None else np.asarray(lens)
+        scale = oa.default_scale(D) if scale is None else scale
+        out = np.full(q.shape, np.nan)
+        lse = np.full((B, Hq, L), np.nan)
+        for b in range(B):
+            n = int(lens[b])
+            for g in range(Hkv):
+                for p in range(n):
+                    lo, hi = first(p, n), max(first(p, n) + 1, min(last(p, n), n))
+                    rows = slice(g * G, (g + 1) * G)
+                    out[b, rows, p], lse[b, rows, p] = oa._attend_rows_ref(q[b, rows, p], k[b, g, lo:hi],
+                                                                           v[b, g, lo:hi], scale)
+        return out, lse
+    return prefill
+
+
 MUTANTS = {
     "dropped_scale": lambda: _with_rows(_rows_no_scale),
     "lse_in_log2": lambda: _with_rows(_rows_log2_lse),
@@ -193,6 +218,11 @@ MUTANTS = {
     "fp8_subnormals_as_normals": lambda: _mutant(fp8_e4m3_value=_fp8_no_subnormals,
                                                  attention_fp8kv=_fp8_with(_fp8_no_subnormals)),
     "fp8_scales_swapped": lambda: _mutant(attention_fp8kv=_fp8_scales_swapped),
+    "prefill_excludes_own_row": lambda: _mutant(prefill_attention=_prefill_window(lambda p, n: 0, lambda p, n: p)),
+    "prefill_one_row_too_many": lambda: _mutant(prefill_attention=_prefill_window(lambda p, n: 0,
+                                                                                 lambda p, n: p + 2)),
+    "prefill_anti_causal": lambda: _mutant(prefill_attention=_prefill_window(lambda p, n: p, lambda p, n: n)),
+    "prefill_not_causal": lambda: _mutant(prefill_attention=_prefill_window(lambda p, n: 0, lambda p, n: n)),
 }
 
 
