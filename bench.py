@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATION_BYTES = 1 << 30
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_PAGED + configs.ALL_FP8 + configs.ALL_BIFURCATED)}
+WORKLOADS = {w.name: w for w in (configs.ALL_DECODE + configs.ALL_PAGED + configs.ALL_FP8 + configs.ALL_BIFURCATED +
+                                  configs.ALL_PREFILL)}
 DEFAULT_WORKLOAD = configs.CODELLAMA34B_SHARE.name
 
 
@@ -286,6 +287,40 @@ def time_variant(w, steps, warmup, force_splits=0):
     return info, None
 
 
+def time_prefill(w, steps, warmup):
+    """Causal prefill of whole sequences: the step is one fd_prefill_attn
+    call; flops = 4 * D * Hq * sum over positions p of (p + 1)."""
+    import torch
+
+    import decode_attention_06_amd as fd
+
+    dev = torch.device("cuda:0")
+    per_copy = (w.batch * (w.q_heads + 2 * w.kv_heads) * w.max_len * w.head_dim) * 2
+    copies = max(2, math.ceil(ROTATION_BYTES / per_copy))
+    sets = []
+    for c in range(copies):
+        s = w.seed + 1000 * c
+        sets.append(tuple(synth.device_normal((w.batch, h, w.max_len, w.head_dim), s + j, "bf16", dev)
+                          for j, h in enumerate((w.q_heads, w.kv_heads, w.kv_heads))))
+    out = torch.empty_like(sets[0][0])
+
+    def step(j):
+        q, k, v = sets[j % copies]
+        fd.prefill_attn(q, k, v, None, out=out)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    eager_ms = timed_eager(step, steps)
+    step_ms = timed_graph(step, steps)
+    L = w.max_len
+    flops = 4 * w.head_dim * w.q_heads * w.batch * (L * (L + 1) // 2)
+    kv_bytes = 2 * w.batch * w.kv_heads * L * w.head_dim * 2
+    info = {"n_splits": None, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": step_ms,
+            "eager_step_ms": eager_ms, "probe_gbs": None, "kernel": "prefill_kernel", "flops": flops}
+    return info, None
+
+
 def time_concatenated(w, sets, dl, steps):
     """Split-KV decode attention over [context ; own decode rows] per sample
     (the non-bifurcated way to get the same result): µs per step."""
@@ -446,7 +481,11 @@ def main():
     fd.load()
     w = WORKLOADS[args.workload]
     bif = w.name in {b.name for b in configs.ALL_BIFURCATED}
-    if bif:
+    prefill = w.name in {x.name for x in configs.ALL_PREFILL}
+    if prefill:
+        info, host = time_prefill(w, args.steps, args.warmup)
+        dtype = w.dtype
+    elif bif:
         info, host = time_bifurcated(w, args.steps, args.warmup, args.compare_concat)
         dtype = w.dtype
     elif getattr(w, "page_size", 0) > 0 or w.dtype == "fp8":
@@ -470,7 +509,10 @@ def main():
     config = {"workload": w.name, "kv_bytes_per_step": info["kv_bytes"], "n_splits": info["n_splits"],
               "input_copies": info["copies"], "timing": "HIP events around a graph replay of the K steps; inputs rotated over >= 1 GiB",
               "eager_us_per_step": round(info["eager_step_ms"] * 1e3, 3)}
-    if bif:
+    if prefill:
+        config.update(batch=w.batch, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                      seq_len=w.max_len, mask="causal")
+    elif bif:
         config.update(samples=w.samples, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
                       ctx_len=w.ctx_len, dec_len=f"{w.dec_lo}..{w.dec_max}")
     else:
@@ -507,6 +549,13 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if prefill:
+        tflops = info["flops"] / step_s / 1e12
+        line.update(value=round(tflops, 2), unit="TFLOP/s", frac_of_hbm_peak=None)
+        line["roofline"] = {"bound": "mfma", "kernel": info["kernel"], "achieved": round(tflops, 2),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "kernel_us": round(info["kernel_ms"] * 1e3, 3), "flops": info["flops"]}
     if "kernel_timing" in info:
         line["roofline"]["kernel_timing"] = info["kernel_timing"]
     if bif:

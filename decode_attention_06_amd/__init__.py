@@ -37,6 +37,8 @@ SIGNATURES = {
                                                    ctypes.POINTER(_c_sz)]),
     "fd_bifurcated_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i64, _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_prefill_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                 _c_vp, _c_i32, _c_vp, _c_f32, _c_vp]),
     "fd_lse_combine": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
     "fd_decode_attn_partials": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                          _c_i32, _c_i32, _c_vp, _c_vp, _c_f32, _c_vp]),
@@ -296,6 +298,38 @@ def bifurcated_attn(q, k_ctx, v_ctx, k_dec, v_dec, dec_lens=None, out=None, out_
                                   _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"),
                                   float(scale), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def prefill_attn(q, k, v, lens=None, out=None, out_dtype=None, scale=0.0, return_lse=False, stream=None):
+    """Causal prefill attention (fd_prefill_attn).
+
+    q [B, Hq, Lmax, D]; k, v [B, Hkv, Lmax, D] (bf16, D 128); lens int32 [B]
+    on the device or None.  Position p attends to cache rows [0, p].
+    Returns out [B, Hq, Lmax, D] (positions past lens[b] untouched) and the
+    natural-log lse [B, Hq, Lmax] when return_lse.
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise FdError(FD_ERR_INVALID_ARG, "expected q [B,Hq,Lmax,D] and k, v [B,Hkv,Lmax,D]")
+    B, Hq, Lmax, D = q.shape
+    if k.shape[0] != B or k.shape[2] != Lmax or k.shape[3] != D:
+        raise FdError(FD_ERR_INVALID_ARG, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise FdError(FD_ERR_UNSUPPORTED, "q, k and v must share one dtype")
+    if lens is not None and (lens.dtype != torch.int32 or lens.shape != (B,)):
+        raise FdError(FD_ERR_INVALID_ARG, "lens must be int32 [B]")
+    if out is None:
+        out = torch.zeros((B, Hq, Lmax, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, Lmax, D):
+        raise FdError(FD_ERR_INVALID_ARG, "out must be [B, Hq, Lmax, D]")
+    lse = torch.full((B, Hq, Lmax), float("nan"), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.fd_prefill_attn(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _opt_ptr(lens, "lens"), B, Hq,
+                               Hkv, D, Lmax, dt, _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"),
+                               float(scale), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

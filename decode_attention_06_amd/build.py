@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfd.so")
 
-SOURCES = ["fd_kernels.hip", "fd_mfma.hip", "fd_bifurcated.hip", "fd_api.cpp"]
+SOURCES = ["fd_kernels.hip", "fd_mfma.hip", "fd_bifurcated.hip", "fd_prefill.hip", "fd_api.cpp"]
 
 # Packed-FP32 instructions stay disabled: ordinary float code only.
 HIP_FLAGS = [

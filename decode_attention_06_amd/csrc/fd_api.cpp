@@ -560,6 +560,43 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     return FD_OK;
 }
 
+fd_status fd_prefill_attn(const void* q, const void* k, const void* v, const int32_t* lens, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype, void* out,
+                          int32_t out_dtype, float* lse_out, float scale, void* stream) {
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, 0));
+    if (dtype != FD_BF16 || D != 128)
+        return fail(FD_ERR_UNSUPPORTED, "prefill supports bf16 with head_dim 128 (got dtype %d, D %d)", dtype, D);
+    if (Hq / Hkv > 128) return fail(FD_ERR_UNSUPPORTED, "prefill supports up to 128 query heads per KV head");
+    FD_TRY(check_out_dtype(out_dtype));
+    FD_TRY(check_ptr(q, 16, "q"));
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    FD_TRY(check_ptr(out, out_dtype == FD_BF16 ? 2 : 4, "out"));
+    if (lens && !aligned(lens, 4)) return fail(FD_ERR_INVALID_ARG, "lens is not 4-byte aligned");
+    if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
+    fd::PrefillParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lens = lens;
+    p.out = out;
+    p.lse_out = lse_out;
+    p.Lmax = Lmax;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.pos_per_tile = 128 / (Hq / Hkv);
+    p.n_ptiles = int32_t((Lmax + p.pos_per_tile - 1) / p.pos_per_tile);
+    p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+    p.out_bf16 = out_dtype == FD_BF16;
+    if (int64_t(B) * Hkv * p.n_ptiles >= (int64_t(1) << 30))
+        return fail(FD_ERR_UNSUPPORTED, "too many prefill work units");
+    hipError_t e = fd::launch_prefill(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return FD_OK;
+}
+
 fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t rows, int32_t n_parts,
                          int32_t D, void* out, int32_t out_dtype, float* lse_out, void* stream) {
     if (rows <= 0 || n_parts <= 0) return fail(FD_ERR_INVALID_ARG, "rows and n_parts must be positive");

@@ -66,6 +66,28 @@ struct BifContextParams {
     float scale_log2;
 };
 
+// Causal prefill on the matrix cores (bf16, head_dim 128): work unit =
+// (sequence b, KV head, tile of pos_per_tile positions); its rows are the
+// pos_per_tile * G (position, head-in-group) pairs.  Position p of sequence
+// b attends to cache rows [0, p]; positions at or beyond lens[b] are not
+// written.
+struct PrefillParams {
+    const void* q;          // [B, Hq, Lmax, D]
+    const void* k;          // [B, Hkv, Lmax, D]
+    const void* v;
+    const int32_t* lens;    // [B] or nullptr = Lmax
+    void* out;              // [B, Hq, Lmax, D]
+    float* lse_out;         // [B, Hq, Lmax] natural-log lse, or nullptr
+    int64_t Lmax;
+    int32_t B, Hq, Hkv;
+    int32_t pos_per_tile;   // 128 / G
+    int32_t n_ptiles;       // ceil(Lmax / pos_per_tile)
+    float scale_log2;
+    int32_t out_bf16;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 int bif_context_waves(int S, int G);        // 8 (one workgroup per CU) or 4
 int bif_context_row_tiles(int S, int G);
 

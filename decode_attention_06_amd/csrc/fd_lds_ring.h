@@ -1,0 +1,159 @@
+// LDS tile ring shared by the kernels that stream one KV range for many
+// query rows (bifurcated context part, prefill): 32-token K/V tiles go
+// straight from global memory into a ring of LDS stages
+// (global_load_lds_dwordx4), every wave of the workgroup reads each tile
+// with the matrix-core operand layouts.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+#include "fd_mfma_common.h"
+
+namespace fd {
+namespace {
+
+constexpr int CTX_TILE = MF_TILE;         // tokens per LDS tile (32)
+constexpr int CTX_STAGES = 4;             // LDS ring: three tiles in flight
+constexpr int CTX_TILE_BYTES = CTX_TILE * 256;
+constexpr int XCDS = 8;
+
+// LDS byte offset of 16-byte chunk c (0..15) of token row t (0..31) in a
+// tile.  The chunk index is XORed with (t & 3) | (bits 3-4 of t) << 2, which
+// makes the K-operand reads (16 lanes: tokens {0..3, 8..11, 16..19, 24..27}
+// + const, one chunk) and the V-block reads (16 lanes: one token, chunks
+// 0..15) touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int t) { return (t & 3) | (((t >> 3) & 3) << 2); }
+__device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ swz(t)) << 4); }
+
+// Issue the loads of one 32-token tile straight into LDS
+// (global_load_lds_dwordx4: lane L of a wave instruction lands at the
+// instruction's LDS base + 16 L).  Wave w fills K and V bytes
+// [2048 w, 2048 w + 2048) of the stage: rows 8w .. 8w+7; lane L of part k
+// writes row 8w + 4k + L/16 at chunk position L%16, so it fetches chunk
+// (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1
+// (c1 > t0 is not required: a tile past the end re-reads row c1 - 1).
+// Addresses are a wave-uniform base (row min(t0, c1 - 1)) plus a 32-bit
+// lane offset below 8 KiB, shared by K and V.  Four vector-memory
+// instructions per wave.
+// Offset registers of one wave's loads for a tile (one per KiB per
+// operand: 4 waves use both, 8 waves the first).
+struct TileAddrs {
+    uint32_t off[2];
+};
+
+template <int NW>
+__device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1,
+                                                    int wave, int lane, char* kst, char* vst) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    constexpr int IPW = 8 / NW;             // 1 KiB loads per wave per operand
+    const int tbase = min(t0, c1 - 1);
+    const uint16_t* kt = kbase + (int64_t)tbase * MF_D;
+    const uint16_t* vt = vbase + (int64_t)tbase * MF_D;
+    TileAddrs a;
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) {
+        const int row = 4 * IPW * wave + 4 * k + (lane >> 4);
+        const int chunk = (lane & 15) ^ swz(row);
+        const int t = min(t0 + row, c1 - 1);
+        const int base = 1024 * (IPW * wave + k);
+        a.off[k] = (uint32_t)((t - tbase) * MF_D + 8 * chunk);
+        __builtin_amdgcn_global_load_lds(kt + a.off[k], (lds_ptr)(kst + base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + a.off[k], (lds_ptr)(vst + base), 16, 0, 0);
+    }
+    return a;
+}
+
+// Keeps the offset registers of the last issued tile alive up to this
+// point (no instruction is emitted), so the registers of the LDS reads that
+// follow the issue are never the in-flight loads' address registers and the
+// compiler needs no wait for them.
+template <int NW>
+__device__ __forceinline__ void keep_addrs(const TileAddrs& a) {
+    if constexpr (NW == 4)
+        asm volatile("" ::"v"(a.off[0]), "v"(a.off[1]));
+    else
+        asm volatile("" ::"v"(a.off[0]));
+}
+
+// V^T operand of output block e (d = 16e .. 16e+15) for lane (g, i): the
+// eight values V[8g + j][16e + i], j = 0..7, from two transposing LDS reads
+// (ds_read_b64_tr_b16: within a 16-lane group, lane 4a + c receives element
+// c of the 64-bit rows addressed by lanes a, a+4, a+8, a+12).  For read h,
+// lane i of group g addresses token 8g + 4h + i/4, columns 16e + 4 (i%4) ..
+// +3, so lane i gets tokens 8g + 4h .. +3 of column 16e + i.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
+
+__device__ __forceinline__ u32x4_t v_operand(const char* __restrict__ rv, int e, int g, int i) {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int t = 8 * g + 4 * h + (i >> 2);
+        const int chunk = 2 * e + ((i & 3) >> 1);
+        const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(rv + lds_off(t, chunk) + 8 * (i & 1)));
+        const u32x2_t w = __builtin_bit_cast(u32x2_t, x);
+        r[2 * h] = w[0];
+        r[2 * h + 1] = w[1];
+    }
+    return r;
+}
+
+// One ring step: issue the loads of a later tile into stage (wk, wv) and
+// read the next tile's operands from stage (rk, rv).  The restrict
+// qualifiers state that the stages are disjoint, which lets the compiler
+// read one stage while the other is still being filled.
+template <int NW>
+__device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint16_t* vbase, int t_issue, int c1,
+                                                   int wave, int lane, char* __restrict__ wk, char* __restrict__ wv,
+                                                   const char* __restrict__ rk, const char* __restrict__ rv, int ktok0,
+                                                   int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vt)[8]) {
+    const TileAddrs a = issue_tile<NW>(kbase, vbase, t_issue, c1, wave, lane, wk, wv);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int tt = ktok0 + 4 * blk;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4_t*>(rk + lds_off(tt, 4 * s + g));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[e] = v_operand(rv, e, g, i);
+    return a;
+}
+
+// One ring tile for a wave's 32 query rows: scores, softmax step (masks as
+// in tile_softmax), then O^T += V^T P^T with the transposed V operands
+// (output row m of block e is d = 16e + m).
+__device__ __forceinline__ void ring_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vt)[8],
+                                          const bf16x8_t (&qb)[2][4], int tb, int tmask, const int (&lim)[2], int g,
+                                          float sl2, float (&m)[2], f32x4_t (&lacc)[2], f32x4_t (&acc)[2][8]) {
+    f32x4_t sc[2][2];
+    tile_scores<2>(kr, qb, sc);
+    bf16x8_t pb[2];
+    tile_softmax<2>(sc, tb, tmask, lim, g, sl2, m, lacc, acc, pb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            acc[r][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[e]), pb[r], acc[r][e], 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (expcnt and
+// lgkmcnt at their maxima): wait until at most N loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the fence __syncthreads() carries: that fence
+// waits for every outstanding vector-memory load, the tiles still in flight
+// included.  The ring needs no more than the barrier itself: each wave has
+// waited for its own loads of the tile about to be read (wait_vm) and has
+// consumed its LDS reads of the tile whose stage is refilled next.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+constexpr int CTX_LDS_BYTES = CTX_STAGES * 2 * CTX_TILE_BYTES;   // 64 KiB
+
+}  // namespace
+}  // namespace fd

@@ -95,10 +95,12 @@ __device__ __forceinline__ void tile_scores(const u32x4_t (&kr)[2][4], const bf1
         }
 }
 
+// tmask (wave-uniform): no token below it is masked for any row of the
+// wave; lim[r]: the lane's row of block r sees tokens below lim[r] only.
 template <int NRB>
-__device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb, int t1, int g, float sl2,
-                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8],
-                                             bf16x8_t (&pb)[NRB]) {
+__device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb, int tmask, const int (&lim)[NRB],
+                                             int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
+                                             f32x4_t (&acc)[NRB][8], bf16x8_t (&pb)[NRB]) {
     // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
     // the very weights used in P V, accumulated in fp32 by the matrix core.
     const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -108,15 +110,15 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
     for (int r = 0; r < NRB; ++r)
 #pragma unroll
         for (int j = 0; j < 8; ++j) t[r][j] = sc[r][j >> 2][j & 3];
-    // Only a piece's last tile can hold tokens at or beyond t1.  The empty
-    // asm statements keep this a branch: folded into selects it would run on
-    // every tile.
-    if (tb + MF_TILE > t1) {
+    // Only tiles reaching tmask hold masked tokens (a piece's last tile, a
+    // causal diagonal).  The empty asm statements keep this a branch: folded
+    // into selects it would run on every tile.
+    if (tb + MF_TILE > tmask) {
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                if (tb + 8 * g + j >= t1) t[r][j] = -INFINITY;
+                if (tb + 8 * g + j >= lim[r]) t[r][j] = -INFINITY;
                 asm volatile("" : "+v"(t[r][j]));
             }
     }
@@ -173,7 +175,10 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
     f32x4_t sc[NRB][2];
     tile_scores<NRB>(kr, qb, sc);
     bf16x8_t pb[NRB];
-    tile_softmax<NRB>(sc, tb, t1, g, sl2, m, lacc, acc, pb);
+    int lim[NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) lim[r] = t1;
+    tile_softmax<NRB>(sc, tb, t1, lim, g, sl2, m, lacc, acc, pb);
     pv_block<0>(vr, pb, acc);
     pv_block<1>(vr, pb, acc);
     pv_block<2>(vr, pb, acc);

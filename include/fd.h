@@ -259,6 +259,28 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
                              void* stream);
 
 /*
+ * fd_prefill_attn - causal many-query (prefill) attention over a whole
+ * sequence ([FD] "Por qué la decodificación necesita otra planificación":
+ * during prefill many query positions run in parallel; [MW] section on why
+ * prompts are fast and generation slow: matrix-matrix work; [FA] on-chip
+ * blocks of queries, keys and values with the online softmax).  Position p
+ * of sequence b attends to cache rows [0, p].
+ *
+ *   q        bf16 [B, Hq, Lmax, D]  one query per position
+ *   k, v     bf16 [B, Hkv, Lmax, D]
+ *   lens     device int32 [B], each in [1, Lmax]; NULL = all Lmax
+ *   out      [B, Hq, Lmax, D] in out_dtype; positions at or beyond lens[b]
+ *            are not written
+ *   lse_out  device fp32 [B, Hq, Lmax] (natural log) or NULL
+ *   scale    softmax temperature; <= 0 selects 1/sqrt(D)
+ * Supported: bf16, head_dim 128, G = Hq / Hkv <= 128.  No workspace.
+ */
+fd_status fd_prefill_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t max_len, int32_t dtype, void* out,
+                          int32_t out_dtype, float* lse_out, float scale, void* stream);
+
+/*
  * fd_lse_combine - the reduction of [FD] on its own: merges per-piece
  * normalised outputs and their natural-log lse into the full result.
  *

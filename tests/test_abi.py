@@ -206,6 +206,27 @@ def test_fp8_dtype_only_through_its_entry_point(lib):
     assert n8.value == n16.value > 0
 
 
+def test_prefill_rejects_before_any_hip_call(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, lens=None, B=1, Hq=16, Hkv=2, D=128, L=1024, dtype=fd.FD_BF16, out=FAKE,
+                 odt=fd.FD_BF16, lse=None, scale=0.0)
+        a.update(kw)
+        return lib.fd_prefill_attn(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["L"],
+                                   a["dtype"], a["out"], a["odt"], a["lse"], a["scale"], None)
+    assert call(dtype=fd.FD_F32) == fd.FD_ERR_UNSUPPORTED
+    assert call(D=64) == fd.FD_ERR_UNSUPPORTED
+    assert call(Hq=256, Hkv=1) == fd.FD_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == fd.FD_ERR_UNSUPPORTED
+    assert call(q=None) == fd.FD_ERR_INVALID_ARG
+    assert call(k=MISALIGNED) == fd.FD_ERR_INVALID_ARG
+    assert call(out=0x10001) == fd.FD_ERR_INVALID_ARG
+    assert call(lens=0x10001) == fd.FD_ERR_INVALID_ARG
+    assert call(L=0) == fd.FD_ERR_INVALID_ARG
+    assert call(B=0) == fd.FD_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == fd.FD_ERR_INVALID_ARG
+    assert call(odt=7) == fd.FD_ERR_UNSUPPORTED
+
+
 def test_bifurcated_rejects_bad_arguments(lib):
     def call(**kw):
         a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=FAKE, vd=FAKE, dl=None, S=4, Hq=8, Hkv=2, D=128, Lc=64, Ld=8,

@@ -9,7 +9,8 @@ from dataclasses import dataclass
 __all__ = ["DecodeWorkload", "BifurcatedWorkload", "TINY", "CODELLAMA34B_SHARE",
            "MHA_SWEEP", "BIFURCATED_MQA", "BIFURCATED_GQA", "CODELLAMA34B_SHARE_PAGED",
            "MHA_B16_L65536_PAGED", "CODELLAMA34B_SHARE_FP8", "MHA_B16_L65536_FP8", "ALL_DECODE",
-           "ALL_BIFURCATED", "ALL_PAGED", "ALL_FP8"]
+           "ALL_BIFURCATED", "ALL_PAGED", "ALL_FP8", "PrefillWorkload", "PREFILL_CODELLAMA34B_SHARE",
+           "PREFILL_MHA", "ALL_PREFILL"]
 
 
 @dataclass(frozen=True)
@@ -88,6 +89,26 @@ CODELLAMA34B_SHARE_FP8 = DecodeWorkload("codellama34b_share_fp8kv_b1_hq16_hkv2_d
                                         1, 16, 2, 128, 65536, "fp8", False, 0, 8, 1e-2)
 MHA_B16_L65536_FP8 = DecodeWorkload("mha_fp8kv_b16_h32_d128_l65536", 16, 32, 32, 128, 65536, "fp8", True, 0,
                                     9, 1e-2)
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    max_len: int
+    dtype: str
+    seed: int
+    tol: float
+
+
+# Causal prefill of a whole prompt: the CodeLlama-34B one-GPU share over 16K
+# tokens, and 32-head MHA over 8K tokens at batch 2.
+PREFILL_CODELLAMA34B_SHARE = PrefillWorkload("prefill_codellama34b_share_b1_hq16_hkv2_d128_l16384_bf16", 1, 16, 2,
+                                             128, 16384, "bf16", 10, 1e-2)
+PREFILL_MHA = PrefillWorkload("prefill_mha_b2_h32_d128_l8192_bf16", 2, 32, 32, 128, 8192, "bf16", 11, 1e-2)
+ALL_PREFILL = (PREFILL_CODELLAMA34B_SHARE, PREFILL_MHA)
 
 ALL_DECODE = (TINY, CODELLAMA34B_SHARE) + MHA_SWEEP
 ALL_PAGED = (CODELLAMA34B_SHARE_PAGED, MHA_B16_L65536_PAGED)
