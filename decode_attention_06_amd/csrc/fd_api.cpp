@@ -34,6 +34,7 @@ fd_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int32_t kWgPerCu = 2;        // partial-kernel workgroups to keep per CU
+constexpr int64_t kFewMfmaUnits = 8;   // at most this many units: one workgroup per CU
 constexpr int64_t kMinChunk = 256;     // shortest piece worth a partial result (vector-ALU kernel)
 constexpr int64_t kMinChunkMfma = 128; // matrix-core kernel: one 32-token tile per wave
 constexpr int64_t kMaxLen = int64_t(1) << 30;
@@ -188,9 +189,9 @@ int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     const int G = num_q_heads / num_kv_heads;
     const Path path = choose_path(dtype, head_dim, G);
     const int64_t units = int64_t(batch) * num_kv_heads * path.row_blocks;
-    // Eight-wave workgroups (few units) fill a CU one at a time.
-    const int64_t wg_per_cu =
-        (path.mfma && fd::mfma_waves_per_unit(int(std::min<int64_t>(units, 1 << 30))) == 8) ? 1 : kWgPerCu;
+    // Very few units (long single sequences) on the matrix-core kernel: one
+    // workgroup per CU, which halves the pieces to combine and reads as fast.
+    const int64_t wg_per_cu = (path.mfma && units <= kFewMfmaUnits) ? 1 : kWgPerCu;
     const int64_t target = int64_t(n_cu) * wg_per_cu;
     if (units >= target) return 1;
     int64_t s = (target + units - 1) / units;

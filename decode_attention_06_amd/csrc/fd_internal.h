@@ -108,12 +108,6 @@ inline int valu_rows_per_block(int G, bool fp8_cache = false) {
 // Rows per work unit of the matrix-core kernel (16 or 32) for a group of G.
 int mfma_rows_per_block(int G);
 
-// Waves per workgroup of the matrix-core partial kernel for a call with this
-// many (sequence, KV head, row block) units: 8 when there are very few units
-// (long single sequences), so each workgroup covers a longer piece and the
-// pieces to combine are fewer; 4 otherwise.
-int mfma_waves_per_unit(int units);
-
 // Matrix-core partial kernel: bf16, head_dim 128, any G (row_blocks =
 // ceil(G / mfma_rows_per_block(G))).
 hipError_t launch_partial_mfma(const PartialParams& p, bool fp8_cache, hipStream_t stream);

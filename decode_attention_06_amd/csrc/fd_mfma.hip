@@ -46,12 +46,9 @@ __global__ __launch_bounds__(64 * NW, (NRB == 1 && NW == 4) ? 2 : 1) void partia
 }
 
 template <bool PAGED, bool KV8>
-hipError_t launch_mfma_layout(const PartialParams& p, dim3 grid, int rows, bool wide, hipStream_t stream) {
+hipError_t launch_mfma_layout(const PartialParams& p, dim3 grid, int rows, hipStream_t stream) {
     if (rows == 16) {
-        if (wide)
-            hipLaunchKernelGGL((partial_mfma_kernel<1, 8, PAGED, KV8>), grid, dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED, KV8>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED, KV8>), grid, dim3(256), 0, stream, p);
     } else {
         hipLaunchKernelGGL((partial_mfma_kernel<2, 4, PAGED, KV8>), grid, dim3(256), 0, stream, p);
     }
@@ -62,20 +59,17 @@ hipError_t launch_mfma_layout(const PartialParams& p, dim3 grid, int rows, bool 
 
 int mfma_rows_per_block(int G) { return G > 16 ? 32 : 16; }
 
-int mfma_waves_per_unit(int units) { return units <= 8 ? 8 : 4; }
-
 hipError_t launch_partial_mfma(const PartialParams& p, bool fp8_cache, hipStream_t stream) {
     const int G = p.Hq / p.Hkv;
     const int rows = mfma_rows_per_block(G);
     if (p.row_blocks != (G + rows - 1) / rows) return hipErrorInvalidValue;
     const int64_t units = (int64_t)p.B * p.Hkv * p.row_blocks;
     const dim3 grid((unsigned)(units * p.n_splits));
-    const bool wide = mfma_waves_per_unit((int)std::min<int64_t>(units, 1 << 30)) == 8;
     if (fp8_cache)
-        return p.block_table ? launch_mfma_layout<true, true>(p, grid, rows, wide, stream)
-                             : launch_mfma_layout<false, true>(p, grid, rows, wide, stream);
-    return p.block_table ? launch_mfma_layout<true, false>(p, grid, rows, wide, stream)
-                         : launch_mfma_layout<false, false>(p, grid, rows, wide, stream);
+        return p.block_table ? launch_mfma_layout<true, true>(p, grid, rows, stream)
+                             : launch_mfma_layout<false, true>(p, grid, rows, stream);
+    return p.block_table ? launch_mfma_layout<true, false>(p, grid, rows, stream)
+                         : launch_mfma_layout<false, false>(p, grid, rows, stream);
 }
 
 }  // namespace fd

@@ -120,19 +120,18 @@ __device__ __forceinline__ PagedTile paged_tile(const PartialParams& p, int b, i
 }
 
 // NRB blocks of 16 query rows per work unit share every K/V load; NW waves
-// per workgroup take interleaved 32-token tiles of the unit's piece.
-// Accumulator element (row, d = 8 (4g + ii) + e) of a wave sits at word
-// row * MF_ACC_STRIDE + acc_col(g, ii, e): with a row stride of 132 words and
-// the lane group g in the low bits of the column, the 64 lanes of one store
-// (rows i = 0..15, groups g = 0..3, fixed ii and e) hit 64 distinct banks,
-// and reads along d conflict at most 2-way.
+// per workgroup take interleaved 32-token tiles of the unit's piece.  The
+// waves' states meet in LDS: per-row max and sum first, then each wave's
+// accumulators already scaled by its weight in the merged sum, at word
+// row * MF_ACC_STRIDE + d.  Lane (g, i) stores d = 32g + 8ii + e0 .. +3 as
+// one 16-byte write; with a row stride of 132 words the 16 lanes of a group
+// (rows i = 0..15) cover all 64 banks.
 constexpr int MF_ACC_STRIDE = MF_D + 4;
-__device__ __forceinline__ int acc_col(int g, int ii, int e) { return 4 * (8 * ii + e) + g; }
 
 template <int NRB, int NW>
 struct PartialLds {
     static constexpr int ROWS = 16 * NRB;
-    float acc[NW][ROWS][MF_ACC_STRIDE];
+    alignas(16) float acc[NW][ROWS][MF_ACC_STRIDE];
     float m[NW][ROWS];
     float l[NW][ROWS];
 };
@@ -241,48 +240,86 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         }
     }
 
-    // Hand the wave state (row sums already complete in lacc) to LDS.
+    // Merge of the waves' states (row sums already complete in lacc).
+    // Every lane computes its rows' merged max M and sum L from the waves'
+    // (m, l) and scales its own accumulators by exp2(m - M) / L in
+    // registers; what is left per output element is a plain sum over waves.
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        const int row = r * 16 + i;
+        if (g == 0 && row < nr) {
+            s_m[wave][row] = m[r];
+            s_l[wave][row] = lacc[r][0];
+        }
+    }
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         const int row = r * 16 + i;
         if (row < nr) {
+            float M = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][row]);
+            float L = 0.f;
+            if (M != -INFINITY) {
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) s_acc[wave][row][acc_col(g, ii, e)] = acc[r][e][ii];
-            if (g == 0) {
-                s_m[wave][row] = m[r];
-                s_l[wave][row] = lacc[r][0];
+                for (int w = 0; w < NW; ++w) L = fmaf(s_l[w][row], fast_exp2(s_m[w][row] - M), L);
+            }
+            const float f = (L > 0.f) ? fast_exp2(m[r] - M) / L * vsc : 0.f;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                for (int e0 = 0; e0 < 8; e0 += 4) {
+                    f32x4_t o;
+                    o[0] = acc[r][e0][ii] * f;
+                    o[1] = acc[r][e0 + 1][ii] * f;
+                    o[2] = acc[r][e0 + 2][ii] * f;
+                    o[3] = acc[r][e0 + 3][ii] * f;
+                    *reinterpret_cast<f32x4_t*>(&s_acc[wave][row][32 * g + 8 * ii + e0]) = o;
+                }
+            if (wave == 0 && g == 0) {
+                const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
+                const int64_t orow = (int64_t)b * p.Hq + h0 + row;
+                if (p.direct) {
+                    if (p.lse_out) p.lse_out[orow] = lse;
+                } else {
+                    p.lse_part[orow * p.part_stride + p.part_offset + split] = lse;
+                }
             }
         }
     }
     __syncthreads();
 
-    for (int x = tid; x < nr * D; x += NW * 64) {
-        const int row = x / D, d = x % D;
-        const int col = acc_col(d >> 5, (d >> 3) & 3, d & 7);
-        float M = -INFINITY;
+    // Four consecutive outputs per thread: the sum of the waves' scaled
+    // accumulators.  Vector stores where the destination allows them.
+    const bool vec_f32 = (reinterpret_cast<uintptr_t>(p.direct ? p.out : p.o_part) & 15) == 0;
+    const bool vec_bf16 = (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
+    for (int x = tid; x < nr * (D / 4); x += NW * 64) {
+        const int row = x / (D / 4), d0 = 4 * (x % (D / 4));
+        f32x4_t a = *reinterpret_cast<const f32x4_t*>(&s_acc[0][row][d0]);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][row]);
-        float L = 0.f, A = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float a = fast_exp2(s_m[w][row] - M);
-                L = fmaf(s_l[w][row], a, L);
-                A = fmaf(s_acc[w][row][col], a, A);
-            }
-        }
-        const float o = (L > 0.f) ? A / L * vsc : 0.f;
-        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
+        for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4_t*>(&s_acc[w][row][d0]);
         const int64_t orow = (int64_t)b * p.Hq + h0 + row;
         if (p.direct) {
-            store_out(p.out, orow * D + d, o, p.out_bf16);
-            if (d == 0 && p.lse_out) p.lse_out[orow] = lse;
+            const int64_t o0 = orow * D + d0;
+            if (p.out_bf16 && vec_bf16) {
+                const uint32_t lo = (uint32_t)to_bf16(a[0]) | ((uint32_t)to_bf16(a[1]) << 16);
+                const uint32_t hi = (uint32_t)to_bf16(a[2]) | ((uint32_t)to_bf16(a[3]) << 16);
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + o0) = u32x2_t{lo, hi};
+            } else if (!p.out_bf16 && vec_f32) {
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + o0) = a;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) store_out(p.out, o0 + k, a[k], p.out_bf16);
+            }
         } else {
-            const int64_t slot = orow * p.part_stride + p.part_offset + split;
-            p.o_part[slot * D + d] = o;
-            if (d == 0) p.lse_part[slot] = lse;
+            float* dst = p.o_part + (orow * p.part_stride + p.part_offset + split) * D + d0;
+            if (vec_f32) {
+                *reinterpret_cast<f32x4_t*>(dst) = a;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dst[k] = a[k];
+            }
         }
     }
 }
