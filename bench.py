@@ -168,20 +168,25 @@ def time_decode(w, steps, warmup, force_splits=0):
     o_part = torch.empty((rows, ns, w.head_dim), dtype=torch.float32, device=dev)
     lse_part = torch.empty((rows, ns), dtype=torch.float32, device=dev)
 
+    ws_bytes = fd.decode_workspace_size(w.batch, w.q_heads, w.kv_heads, w.head_dim, w.max_len, dt, ns)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
     def step(j):
         q, k, v = sets[j % copies]
-        if ns == 1:
-            fd.decode_attn(q, k, v, lens, n_splits=1, out=out, workspace=o_part)
-        else:
-            fd.decode_attn_partials(q, k, v, ns, lens=lens, o_part=o_part, lse_part=lse_part)
-            fd.lse_combine(o_part.view(rows, ns, w.head_dim), lse_part, out=out.view(rows, w.head_dim))
+        fd.decode_attn(q, k, v, lens, n_splits=ns, out=out, workspace=ws)
+
+    # The partial kernel alone, exactly as the step launches it (pieces
+    # interleaved on the matrix-core kernel), for the roofline of the
+    # dominant kernel.
+    mfma = w.dtype == "bf16" and w.head_dim == 128 and w.q_heads // w.kv_heads >= 4
+    layout = fd.FD_PIECES_INTERLEAVED if mfma else fd.FD_PIECES_CONTIGUOUS
 
     def partial_only(j):
         q, k, v = sets[j % copies]
         if ns == 1:
-            fd.decode_attn(q, k, v, lens, n_splits=1, out=out, workspace=o_part)
+            fd.decode_attn(q, k, v, lens, n_splits=1, out=out, workspace=ws)
         else:
-            fd.decode_attn_partials(q, k, v, ns, lens=lens, o_part=o_part, lse_part=lse_part)
+            fd.decode_attn_partials(q, k, v, ns, lens=lens, o_part=o_part, lse_part=lse_part, layout=layout)
 
     for j in range(warmup):
         step(j)
@@ -204,8 +209,7 @@ def time_decode(w, steps, warmup, force_splits=0):
     info = {
         "n_splits": ns, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": kern_ms,
         "eager_step_ms": eager_ms, "probe_gbs": probe_bytes / (probe_ms * 1e-3) / 1e9,
-        "kernel": "partial_mfma_kernel" if (w.dtype == "bf16" and w.head_dim == 128 and
-                                             w.q_heads // w.kv_heads >= 4) else "partial_valu_kernel",
+        "kernel": "partial_mfma_kernel" if mfma else "partial_valu_kernel",
         "flops": 4 * int(lens.sum().item()) * w.q_heads * w.head_dim,
     }
     host = [t.detach().float().cpu().numpy() for t in sets[0]]

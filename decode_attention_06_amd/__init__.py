@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libf
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
 FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
 FD_MAX_SPLITS = 4096
+FD_PIECES_CONTIGUOUS, FD_PIECES_INTERLEAVED = 0, 1
 
 # Exported symbols and their ctypes signatures (mirrors include/fd.h).
 _c_i32, _c_i64, _c_sz, _c_vp, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -40,8 +41,9 @@ SIGNATURES = {
     "fd_prefill_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                  _c_vp, _c_i32, _c_vp, _c_f32, _c_vp]),
     "fd_lse_combine": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "fd_piece_tile_rows": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "fd_decode_attn_partials": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
-                                         _c_i32, _c_i32, _c_vp, _c_vp, _c_f32, _c_vp]),
+                                         _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_f32, _c_vp]),
     "fd_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_vp]),
 }
 
@@ -348,8 +350,15 @@ def lse_combine(o_part, lse_part, out=None, out_dtype=None, return_lse=False, st
     return (out, lse) if return_lse else out
 
 
-def decode_attn_partials(q, k, v, n_splits, lens=None, o_part=None, lse_part=None, scale=0.0, stream=None):
-    """fd_decode_attn_partials: per-piece outputs [B*Hq, n_splits, D] and lse [B*Hq, n_splits]."""
+def piece_tile_rows(q_heads, kv_heads, head_dim, dtype):
+    """fd_piece_tile_rows: rows per tile of the interleaved piece layout (-1: invalid)."""
+    return load().fd_piece_tile_rows(q_heads, kv_heads, head_dim, dtype)
+
+
+def decode_attn_partials(q, k, v, n_splits, lens=None, o_part=None, lse_part=None, scale=0.0, stream=None,
+                         layout=FD_PIECES_CONTIGUOUS):
+    """fd_decode_attn_partials: per-piece outputs [B*Hq, n_splits, D] and lse [B*Hq, n_splits].
+    layout: FD_PIECES_CONTIGUOUS (0) or FD_PIECES_INTERLEAVED (1)."""
     torch = _torch()
     lib = load()
     B, Hq, D = q.shape
@@ -362,7 +371,7 @@ def decode_attn_partials(q, k, v, n_splits, lens=None, o_part=None, lse_part=Non
         lse_part = torch.empty((rows, n_splits), dtype=torch.float32, device=q.device)
     _check(lib.fd_decode_attn_partials(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
                                        _opt_ptr(lens, "lens"), B, Hq, Hkv, D, Lmax, dt, int(n_splits),
-                                       _dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"),
+                                       int(layout), _dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"),
                                        float(scale), _stream(stream)))
     return o_part, lse_part
 

@@ -290,6 +290,10 @@ static fd_status run_decode(fd::PartialParams p, const void* q, const int32_t* l
     p.scale_log2 = resolve_scale(scale, D) * kLog2e;
     p.out_bf16 = out_dtype == FD_BF16;
     p.direct = ns == 1;
+    // Several pieces on the matrix-core kernel: interleaved workgroup steps
+    // (the combine does not depend on which rows a piece holds).  The
+    // vector-ALU kernel streams long contiguous pieces faster.
+    p.strided = path.mfma && ns > 1;
     float* lse_part = nullptr;
     float* o_part = nullptr;
     if (ns > 1) {
@@ -381,13 +385,25 @@ fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v
                       workspace, workspace_bytes, stream);
 }
 
+int32_t fd_piece_tile_rows(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        (head_dim != 64 && head_dim != 128) || (dtype != FD_F32 && dtype != FD_BF16 && dtype != FD_FP8_E4M3))
+        return -1;
+    const Path path = choose_path(dtype, head_dim, num_q_heads / num_kv_heads);
+    if (path.mfma) return fd::MFMA_TILE_ROWS;
+    const int elem = dtype == FD_F32 ? 4 : dtype == FD_BF16 ? 2 : 1;
+    return fd::valu_tile_rows(elem, head_dim, path.rows_per_block);
+}
+
 fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, const int32_t* lens,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
-                                  int32_t dtype, int32_t n_splits, float* o_part, float* lse_part,
-                                  float scale, void* stream) {
+                                  int32_t dtype, int32_t n_splits, int32_t piece_layout, float* o_part,
+                                  float* lse_part, float scale, void* stream) {
     if (dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "the partial stage takes fp32 or bf16 caches");
     FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
     if (n_splits <= 0) return fail(FD_ERR_INVALID_ARG, "n_splits must be given (> 0) for the partial stage");
+    if (piece_layout != FD_PIECES_CONTIGUOUS && piece_layout != FD_PIECES_INTERLEAVED)
+        return fail(FD_ERR_INVALID_ARG, "piece_layout %d is neither contiguous (0) nor interleaved (1)", piece_layout);
     FD_TRY(check_ptr(q, 16, "q"));
     FD_TRY(check_ptr(k, 16, "k"));
     FD_TRY(check_ptr(v, 16, "v"));
@@ -412,6 +428,7 @@ fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, c
     p.row_blocks = path.row_blocks;
     p.scale_log2 = resolve_scale(scale, D) * kLog2e;
     p.direct = 0;
+    p.strided = piece_layout == FD_PIECES_INTERLEAVED;
     p.o_part = o_part;
     p.lse_part = lse_part;
     p.part_stride = n_splits;

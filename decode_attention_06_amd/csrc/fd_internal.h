@@ -34,6 +34,10 @@ struct PartialParams {
     float scale_log2;       // softmax scale * log2(e)
     int32_t out_bf16;       // direct mode output dtype
     int32_t direct;         // 1: n_splits == 1, write the final output
+    // Piece layout: 0 gives piece i the contiguous rows [i*c, (i+1)*c); 1
+    // deals the kernel's workgroup steps (MFMA_TILE_ROWS or valu_tile_rows
+    // rows) out round-robin, piece i taking steps i, i + n_splits, ...
+    int32_t strided;
     // Paged cache (block_table != nullptr): row t of (b, kvh) is row
     // t & (page_size - 1) of page block_table[b * bt_stride + (t >> page_shift)],
     // at element page * page_stride + kvh * kv_stride_h + (t & (page_size - 1)) * D.
@@ -104,6 +108,19 @@ inline int valu_rows_per_block(int G, bool fp8_cache = false) {
     const int r = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     return (fp8_cache && r > 4) ? 4 : r;
 }
+
+// Cache rows per workgroup step of the vector-ALU partial kernel, for
+// elements of elem_bytes, head_dim D and GB query rows per unit: 4 waves,
+// each loading 64 / (D / (16 / elem_bytes)) rows per 16-byte-per-lane load
+// with U loads in flight (8 for GB <= 2, else 4; halved for 1-byte
+// elements).  The interleaved piece layout deals these steps out.
+constexpr int valu_tile_rows(int elem_bytes, int D, int GB) {
+    return 4 * (64 / (D / (16 / elem_bytes))) * (((GB <= 2) ? 8 : 4) / (elem_bytes == 1 ? 2 : 1));
+}
+
+// Cache rows per workgroup step of the matrix-core partial kernel: 4 waves
+// of 32-row tiles.
+constexpr int MFMA_TILE_ROWS = 128;
 
 // Rows per work unit of the matrix-core kernel (16 or 32) for a group of G.
 int mfma_rows_per_block(int G);

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     constexpr int WAVE_TOK = RPW * U;
     constexpr int WG_TOK = NW * WAVE_TOK;
     static_assert(LPR * RPW == 64, "row groups must tile the wave");
+    static_assert(WG_TOK == valu_tile_rows(16 / EPL, D, GB), "workgroup step as the host computes it");
 
     __shared__ float s_acc[NW][GB][D];
     __shared__ float s_m[NW][GB];
@@ -144,13 +145,24 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     const int b = idx / p.Hkv;
     const int h0 = kvh * (GB * p.row_blocks) + rb * GB;
 
-    // Valid rows of this sequence and this unit's piece [t0, t1).  The piece
-    // length is ceil(n / n_splits) rounded up to 16 rows.
+    // Valid rows of this sequence and this unit's piece: the contiguous
+    // rows [t0, t1), ceil(n / n_splits) rounded up to 16 long, walked in
+    // workgroup tiles of WG_TOK rows; or, interleaved, the workgroup tiles
+    // split, split + n_splits, ... of the whole sequence (t1 = n), so that
+    // the grid sweeps one window of the cache at a time.
     int n = p.lens ? p.lens[b] : (int)p.Lmax;
     n = max(0, min(n, (int)p.Lmax));
-    const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
-    const int t0 = (int)min((int64_t)split * chunk, (int64_t)n);
-    const int t1 = min(t0 + chunk, n);
+    int t0, t1, wg_step;
+    if (p.strided) {
+        t0 = (int)min((int64_t)split * WG_TOK, (int64_t)n);
+        t1 = n;
+        wg_step = p.n_splits * WG_TOK;
+    } else {
+        const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
+        t0 = (int)min((int64_t)split * chunk, (int64_t)n);
+        t1 = min(t0 + chunk, n);
+        wg_step = WG_TOK;
+    }
 
     // Query slice of this lane, pre-multiplied by scale*log2(e) (and the
     // KV head's K scale for an E4M3 cache) so that exp2 of a score
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
             kr[u] = *reinterpret_cast<const uint4*>(kpool + gb[h] + off);
             vr[u] = *reinterpret_cast<const uint4*>(vpool + gb[h] + off);
         }
-        if constexpr (PAGED) lookup(tb + WG_TOK);
+        if constexpr (PAGED) lookup(tb + wg_step);
     };
 
     // Scores, online-softmax update and P.V for one loaded wave tile.
@@ -297,28 +309,28 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         if (tb0 < t1) {
             if constexpr (PAGED) lookup(tb0);
             uint4 ka[U], va[U];
-            for (int tb = tb0; tb < t1; tb += WG_TOK) {
+            for (int tb = tb0; tb < t1; tb += wg_step) {
                 load(tb, ka, va);
                 compute(tb, ka, va);
             }
         }
     } else if (tb0 < t1) {
-        const int ntiles = (t1 - tb0 + WG_TOK - 1) / WG_TOK;
+        const int ntiles = (t1 - tb0 + wg_step - 1) / wg_step;
         uint4 ka[U], va[U], kn[U], vn[U];
         if constexpr (PAGED) lookup(tb0);
         load(tb0, ka, va);
-        load(tb0 + WG_TOK, kn, vn);
+        load(tb0 + wg_step, kn, vn);
         int tb = tb0;
         for (int it = 0; it < ntiles / 2; ++it) {
             compute(tb, ka, va);
             __builtin_amdgcn_sched_barrier(0);
-            load(tb + 2 * WG_TOK, ka, va);
+            load(tb + 2 * wg_step, ka, va);
             __builtin_amdgcn_sched_barrier(0);
-            compute(tb + WG_TOK, kn, vn);
+            compute(tb + wg_step, kn, vn);
             __builtin_amdgcn_sched_barrier(0);
-            load(tb + 3 * WG_TOK, kn, vn);
+            load(tb + 3 * wg_step, kn, vn);
             __builtin_amdgcn_sched_barrier(0);
-            tb += 2 * WG_TOK;
+            tb += 2 * wg_step;
         }
         if (ntiles & 1) compute(tb, ka, va);
     }

@@ -41,6 +41,7 @@ namespace {
 
 template <int NRB, int NW, bool PAGED, bool KV8>
 __global__ __launch_bounds__(64 * NW, (NRB == 1 && NW == 4) ? 2 : 1) void partial_mfma_kernel(const PartialParams p) {
+    static_assert(NW * MF_TILE == MFMA_TILE_ROWS, "workgroup step as the host computes it");
     __shared__ PartialLds<NRB, NW> sh;
     partial_mfma_body<NRB, NW, PAGED, KV8>(p, blockIdx.x, sh);
 }

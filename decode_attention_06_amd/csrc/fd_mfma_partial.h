@@ -163,9 +163,23 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
 
     int n = p.lens ? p.lens[b] : (int)p.Lmax;
     n = max(0, min(n, (int)p.Lmax));
-    const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
-    const int t0 = (int)min((int64_t)split * chunk, (int64_t)n);
-    const int t1 = min(t0 + chunk, n);
+    // This piece's rows: the contiguous chunk [t0, t1), read by the waves in
+    // tiles t0 + (k * NW + wave) * 32; or, interleaved, the workgroup steps
+    // split, split + n_splits, ... of NW * 32 rows of the whole sequence.
+    // Interleaved, the whole grid sweeps one window of the cache at a time,
+    // which the memory serves faster than every workgroup streaming its own
+    // chunk.
+    int t0, t1, step;
+    if (p.strided) {
+        t0 = (int)min((int64_t)split * NW * MF_TILE, (int64_t)n);
+        t1 = n;
+        step = p.n_splits * NW * MF_TILE;
+    } else {
+        const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
+        t0 = (int)min((int64_t)split * chunk, (int64_t)n);
+        t1 = min(t0 + chunk, n);
+        step = NW * MF_TILE;
+    }
 
     // Q^T fragments (B operand of the score product); rows >= nr are zero.
     // k-step s of lane group g covers d = 32s + 8g .. +8 (bf16 cache) or
@@ -208,7 +222,6 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // even past the piece's end (its rows clamp to t1 - 1, cache hits), so
     // every path leaves the same number of loads outstanding and the wait
     // before each tile covers only that tile's own loads.
-    constexpr int STEP = NW * MF_TILE;
     Tile ta, tn;
     // Paged: `ahead` holds the page ids of the next tile to load.
     PagedTile ahead{};
@@ -219,7 +232,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
             const int64_t o0 = kv_page_offset<MF_D>(p, ahead.id0, kvh, ahead.s0) - (int64_t)ahead.s0 * MF_D;
             const int64_t o1 = kv_page_offset<MF_D>(p, ahead.id1, kvh, ahead.s1) - (int64_t)ahead.s1 * MF_D;
             load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, at, t1 - 1, ktok0, g, i, r);
-            ahead = paged_tile(p, b, at + STEP, t1 - 1);
+            ahead = paged_tile(p, b, at + step, t1 - 1);
         } else {
             load_rows(kpool, vpool, slice, slice, at, t1 - 1, ktok0, g, i, r);
         }
@@ -229,13 +242,13 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         if constexpr (PAGED) ahead = paged_tile(p, b, tb, t1 - 1);
         load(tb, ta);
         while (true) {
-            load(tb + STEP, tn);
+            load(tb + step, tn);
             compute_loaded<NRB>(ta, qb, tb, t1, g, sl2, m, lacc, acc);
-            tb += STEP;
+            tb += step;
             if (tb >= t1) break;
-            load(tb + STEP, ta);
+            load(tb + step, ta);
             compute_loaded<NRB>(tn, qb, tb, t1, g, sl2, m, lacc, acc);
-            tb += STEP;
+            tb += step;
             if (tb >= t1) break;
         }
     }

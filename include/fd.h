@@ -85,6 +85,23 @@ typedef enum fd_dtype {
  * decode pieces for the bifurcated call). */
 #define FD_MAX_SPLITS 4096
 
+/* Which cache rows make up piece i of a sequence of n valid rows cut into
+ * P pieces ([FD] "Por qué la decodificación necesita otra planificación"
+ * leaves the cut open: any partition of the rows combines to the same
+ * attention).
+ *   FD_PIECES_CONTIGUOUS: rows [i*c, min((i+1)*c, n)), c = ceil(n / P)
+ *     rounded up to a multiple of 16.
+ *   FD_PIECES_INTERLEAVED: the tiles of T rows (T = fd_piece_tile_rows())
+ *     numbered i, i + P, i + 2P, ..., each clipped to [0, n); at any moment
+ *     all pieces then read one window of the cache.
+ * fd_decode_attn (and its paged and E4M3 forms) cuts interleaved where the
+ * matrix-core kernel runs (bf16 or E4M3 cache, head_dim 128, G >= 4) and
+ * contiguous elsewhere: the faster of the two for each kernel. */
+typedef enum fd_piece_layout {
+    FD_PIECES_CONTIGUOUS = 0,
+    FD_PIECES_INTERLEAVED = 1
+} fd_piece_layout;
+
 /* Human-readable name of a status code (static string). */
 const char* fd_status_string(fd_status status);
 
@@ -147,7 +164,8 @@ fd_status fd_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *            size is 0); 256-byte alignment recommended
  *   stream   hipStream_t or NULL
  *
- * The result for fixed inputs and a fixed n_splits is bitwise repeatable
+ * Pieces are cut as fd_piece_layout describes.  The result for fixed
+ * inputs and a fixed n_splits is bitwise repeatable
  * (fixed reduction order, no float atomics).
  */
 fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int32_t* lens,
@@ -208,6 +226,15 @@ fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v
                                size_t workspace_bytes, void* stream);
 
 /*
+ * fd_piece_tile_rows - rows per tile T of the FD_PIECES_INTERLEAVED layout
+ * for these shapes (the partial kernel's rows per workgroup step: 128 on
+ * the matrix-core path; 32 to 256 on the vector-ALU path, depending on the
+ * element size, head_dim and the query rows per unit).  Pure host
+ * function; -1 for invalid or unsupported arguments.
+ */
+int32_t fd_piece_tile_rows(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
+/*
  * fd_decode_attn_partials - the partial stage of fd_decode_attn on its own
  * ([FD] "Por qué la decodificación necesita otra planificación": every piece
  * yields a partial output and its log-sum-exp).  Together with
@@ -216,17 +243,17 @@ fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v
  * history across several devices combine the pieces of all of them.
  *
  *   q, k, v, lens, shapes, dtype, scale: as in fd_decode_attn
- *   n_splits  pieces per sequence, > 0 (no planner here)
- *   o_part    device fp32 [B*Hq, n_splits, D], 16-byte aligned; piece i of
- *             row (b, h) covers cache rows [i*c, min((i+1)*c, lens[b])) with
- *             c = ceil(lens[b] / n_splits) rounded up to a multiple of 16
- *   lse_part  device fp32 [B*Hq, n_splits]; -inf (with o_part = 0) marks an
- *             empty piece
+ *   n_splits      pieces per sequence, > 0 (no planner here)
+ *   piece_layout  fd_piece_layout: which rows each piece covers
+ *   o_part        device fp32 [B*Hq, n_splits, D], 16-byte aligned
+ *   lse_part      device fp32 [B*Hq, n_splits]; -inf (with o_part = 0)
+ *                 marks an empty piece
  */
 fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, const int32_t* lens,
                                   int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int64_t max_len, int32_t dtype, int32_t n_splits,
-                                  float* o_part, float* lse_part, float scale, void* stream);
+                                  int32_t piece_layout, float* o_part, float* lse_part, float scale,
+                                  void* stream);
 
 /*
  * fd_bifurcated_attn_workspace_size - bytes of workspace fd_bifurcated_attn

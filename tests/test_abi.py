@@ -195,8 +195,8 @@ def test_fp8_rejects_before_any_hip_call(lib, kw, status):
 def test_fp8_dtype_only_through_its_entry_point(lib):
     assert _decode(lib, dtype=fd.FD_FP8_E4M3, D=128, Hq=8, Hkv=2) == fd.FD_ERR_UNSUPPORTED
     assert _paged(lib, dtype=fd.FD_FP8_E4M3) == fd.FD_ERR_UNSUPPORTED
-    assert lib.fd_decode_attn_partials(FAKE, FAKE, FAKE, None, 1, 8, 2, 128, 512, fd.FD_FP8_E4M3, 4, FAKE, FAKE,
-                                       0.0, None) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_decode_attn_partials(FAKE, FAKE, FAKE, None, 1, 8, 2, 128, 512, fd.FD_FP8_E4M3, 4, 0, FAKE,
+                                       FAKE, 0.0, None) == fd.FD_ERR_UNSUPPORTED
     # planner and workspace size accept it (same partial layout as bf16)
     assert fd.plan_splits(1, 16, 2, 128, 65536, fd.FD_FP8_E4M3, 256) == fd.plan_splits(1, 16, 2, 128, 65536,
                                                                                        fd.FD_BF16, 256)
@@ -276,3 +276,27 @@ def test_no_device_is_reported_not_fatal(lib):
     assert lib.fd_last_error_message().decode()
     # the planner path of the real call reports the same, without aborting
     assert _decode(lib, n_splits=0) == fd.FD_ERR_HIP
+
+
+def test_piece_tile_rows():
+    # matrix-core kernel: 4 waves of 32-row tiles
+    assert fd.piece_tile_rows(16, 2, 128, fd.FD_BF16) == 128
+    assert fd.piece_tile_rows(64, 2, 128, fd.FD_FP8_E4M3) == 128
+    # vector-ALU kernel: 4 waves x (64 lanes / lanes per row) x loads in flight
+    assert fd.piece_tile_rows(32, 32, 128, fd.FD_BF16) == 4 * 4 * 8     # 8 bf16 per lane, 16 lanes per row
+    assert fd.piece_tile_rows(4, 4, 64, fd.FD_F32) == 4 * 4 * 8         # 4 fp32 per lane, 16 lanes per row
+    assert fd.piece_tile_rows(8, 8, 64, fd.FD_BF16) == 4 * 8 * 8        # 8 lanes per row
+    assert fd.piece_tile_rows(32, 32, 128, fd.FD_FP8_E4M3) == 4 * 8 * 4 # 16 codes per lane, half the loads
+    assert fd.piece_tile_rows(12, 4, 128, fd.FD_BF16) == 4 * 4 * 8     # G 3: one query row per unit
+    assert fd.piece_tile_rows(8, 2, 64, fd.FD_BF16) == 4 * 8 * 4        # 4 rows per unit: 4 loads in flight
+    assert fd.piece_tile_rows(8, 1, 128, fd.FD_F32) == 4 * 2 * 4        # 32 lanes per row, 8 rows per unit
+    for bad in [(0, 1, 128, fd.FD_BF16), (6, 4, 128, fd.FD_BF16), (8, 8, 96, fd.FD_BF16), (8, 8, 128, 7)]:
+        assert fd.piece_tile_rows(*bad) == -1
+
+
+def test_partials_reject_unknown_piece_layout(lib):
+    for layout in (-1, 2):
+        st = lib.fd_decode_attn_partials(FAKE, FAKE, FAKE, None, 1, 8, 2, 128, 512, fd.FD_BF16, 4, layout, FAKE,
+                                         FAKE, 0.0, None)
+        assert st == fd.FD_ERR_INVALID_ARG
+        assert "piece_layout" in lib.fd_last_error_message().decode()

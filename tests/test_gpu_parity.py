@@ -134,6 +134,59 @@ def test_lse_combine_matches_oracle(fd, rows, P, D):
     assert max_abs(to_host(l), ref_l) <= 1e-5
 
 
+# ------------------------------------------------------- partial stage
+
+def piece_rows(layout, n, n_splits, i, tile):
+    """Cache rows of piece i as include/fd.h defines the two layouts."""
+    if layout == 0:
+        c = -(-n // n_splits)
+        c = -(-c // 16) * 16
+        return np.arange(min(i * c, n), min((i + 1) * c, n))
+    tiles = range(i, -(-n // tile), n_splits)
+    return np.concatenate([np.arange(j * tile, min((j + 1) * tile, n)) for j in tiles] or [np.arange(0)])
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["contiguous", "interleaved"])
+@pytest.mark.parametrize("shape,n_splits", [
+    # (B, Hq, Hkv, D, Lmax, dtype, lens), pieces
+    ((2, 16, 2, 128, 3000, "bf16", [3000, 1111]), 7),   # matrix-core kernel, G = 8
+    ((2, 64, 2, 128, 2000, "bf16", [2000, 5]), 4),      # G = 32: 32-row units; pieces past a short sequence
+    ((2, 8, 8, 128, 1500, "bf16", [1500, 700]), 5),     # vector-ALU kernel (MHA)
+    ((2, 8, 2, 64, 1800, "bf16", [1800, 333]), 3),      # vector-ALU, D 64, 4-row units
+    ((1, 4, 4, 64, 512, "fp32", None), 4),              # fp32, D 64
+], ids=lambda s: str(s))
+def test_partials_pieces_match_oracle(fd, shape, n_splits, layout):
+    """fd_decode_attn_partials on its own: each piece's output and lse
+    against the oracle's attention over exactly the rows the layout assigns
+    it (-inf and 0 for an empty piece)."""
+    B, Hq, Hkv, D, L, dtype, lens = shape
+    case = synth.decode_case(B, Hq, Hkv, D, L, dtype, seed=70 + Hq, lens=lens)
+    q, k, v = (to_dev(case[x], dtype) for x in ("q", "k", "v"))
+    lens_d = torch.from_numpy(case["lens"]).to("cuda")
+    o_part, lse_part = fd.decode_attn_partials(q, k, v, n_splits, lens=lens_d, layout=layout)
+    torch.cuda.synchronize()
+    o_h = to_host(o_part).reshape(B, Hq, n_splits, D)
+    l_h = to_host(lse_part).reshape(B, Hq, n_splits)
+    G = Hq // Hkv
+    tile = fd.piece_tile_rows(Hq, Hkv, D, fd.FD_BF16 if dtype == "bf16" else fd.FD_F32)
+    assert tile > 0
+    worst = 0.0
+    for b in range(B):
+        n = int(case["lens"][b])
+        for i in range(n_splits):
+            sel = piece_rows(layout, n, n_splits, i, tile)
+            for g in range(Hkv):
+                rows = slice(g * G, (g + 1) * G)
+                if sel.size == 0:
+                    assert np.all(np.isneginf(l_h[b, rows, i])) and np.all(o_h[b, rows, i] == 0.0)
+                    continue
+                ro, rl = oracle.split_partials(case["q"][b, rows], case["k"][b, g, sel], case["v"][b, g, sel],
+                                               [0, sel.size])
+                worst = max(worst, max_abs(o_h[b, rows, i], ro[0]), max_abs(l_h[b, rows, i], rl[0]))
+    print(f"  tile {tile}, worst max-abs {worst:.3e}", flush=True)
+    assert worst <= TOL[dtype]
+
+
 # ------------------------------------------------------------ bifurcated
 
 @pytest.mark.parametrize("shape", [
