@@ -131,9 +131,14 @@ hipError_t launch_partial(const fd::PartialParams& p, const Path& path, int32_t 
 constexpr int64_t kMinContextPiece = 256;   // shortest context piece planned
 
 // Pieces for the context and for the decode part of a bifurcated call.  The
-// matrix-core context kernel (bf16, D 128) works on tiles of query rows;
-// its piece count fills about two workgroups per CU.  Otherwise the context
-// goes through the split-KV kernel like a batch of S sequences.
+// matrix-core context kernel (bf16, D 128) works on tiles of query rows and
+// shares its launch with the decode units (one piece each).  Of the two
+// workgroup slots per CU, the context units take what the decode units leave
+// but at least three quarters: the decode units then stream their rows from
+// HBM beside the context units from the start, and the context pieces stay
+// long enough that their partials (one per row and piece, written and read
+// back by the combine) cost little.  Otherwise the context goes through the
+// split-KV kernel like a batch of S sequences.
 struct BifPlan {
     bool mfma_ctx;
     int32_t row_tiles;
@@ -147,8 +152,10 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
     if (b.mfma_ctx) {
         b.row_tiles = fd::bif_context_row_tiles(S, Hq / Hkv);
         const int64_t units = int64_t(Hkv) * b.row_tiles;
-        const int64_t wg_per_cu = fd::bif_context_waves(S, Hq / Hkv) == 8 ? 1 : kWgPerCu;
-        int64_t pc = (int64_t(n_cu) * wg_per_cu + units - 1) / units;
+        const int64_t slots = int64_t(n_cu) * kWgPerCu;
+        const int64_t dec_units = int64_t(S) * Hkv * ((Hq / Hkv + 15) / 16);
+        const int64_t ctx_wgs = std::max<int64_t>(slots * 3 / 4, slots - dec_units);
+        int64_t pc = (ctx_wgs + units - 1) / units;
         pc = std::min<int64_t>(pc, std::max<int64_t>(1, Lc / kMinContextPiece));
         b.pc = int32_t(std::max<int64_t>(1, std::min<int64_t>(pc, FD_MAX_SPLITS)));
         // The decode units run beside the context units in the same launch:

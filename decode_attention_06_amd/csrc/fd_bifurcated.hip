@@ -112,9 +112,9 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
     if (c0 < c1) {
         const int n_tiles = (c1 - c0 + CTX_TILE - 1) / CTX_TILE;
         const int lim[2] = {c1, c1};
-        // The query fragments are in registers before the ring starts, so the
-        // waits below count tile loads only.
-        wait_vm<0>();
+        // The query loads were issued before the first tiles' and complete
+        // before them (loads return in order), so the first wait below also
+        // covers them; their latency overlaps the tiles'.
         u32x4_t kr[2][4], vt[8];
 #pragma unroll
         for (int t = 0; t < CTX_STAGES - 1; ++t)
@@ -203,10 +203,8 @@ __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextPara
 
 }  // namespace
 
-int bif_context_waves(int, int) { return 4; }
-
 int bif_context_row_tiles(int S, int G) {
-    const int rows = 32 * bif_context_waves(S, G);
+    constexpr int rows = 32 * 4;   // four waves of 32 rows
     return (S * G + rows - 1) / rows;
 }
 

@@ -92,7 +92,7 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
-int bif_context_waves(int S, int G);        // 8 (one workgroup per CU) or 4
+// Tiles of 128 query rows (four waves of 32) over the S * G rows of a KV head.
 int bif_context_row_tiles(int S, int G);
 
 // Whole bifurcated partial stage in one launch: context units (c) and the

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // The ring as in the bifurcated context part, over rows [0, p_end).
     const int c1 = p_end;
     const int n_tiles = (c1 + CTX_TILE - 1) / CTX_TILE;
-    wait_vm<0>();
+    // The query loads complete before the first tiles' (loads return in
+    // order): the first wait below covers them too.
     u32x4_t kr[2][4], vt[8];
 #pragma unroll
     for (int t = 0; t < CTX_STAGES - 1; ++t) issue_tile<PF_NW>(kbase, vbase, t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
