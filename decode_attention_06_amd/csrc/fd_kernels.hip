@@ -394,7 +394,9 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 }
 
 // LSE combine ([FD] "Por qué la decodificación necesita otra
-// planificación": the reduction that renormalises the pieces).  One
+// planificación": the reduction that renormalises the pieces), general
+// form for head dims that are not a multiple of 4 or an unaligned o_part
+// (lse_combine_v4_kernel below serves the rest).  One
 // workgroup per (row, slice of CMB_SLICE columns); thread (part group pg,
 // column vector dv) handles pieces pg, pg + GROUPS, ...  The first batch of
 // partial outputs is requested together with the row's lse values, so a row
@@ -544,6 +546,109 @@ __global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* _
     }
 }
 
+// LSE combine with 16-byte columns (head_dim a multiple of 4, o_part
+// 16-byte aligned): one workgroup per (row, 32 columns).  Thread (piece
+// group pg = tid / 8, column vector cv = tid % 8) holds pieces pg, pg + 32,
+// pg + 64, pg + 96 of the current batch of 128, their lse and their four
+// columns, all requested in one round trip.  The row maximum takes one wave
+// reduction and one barrier; the weighted sums reduce over the eight piece
+// groups of a wave by three butterfly steps (lanes 8 apart) and over the
+// four waves through LDS.  Every sum runs in a fixed order.
+constexpr int CMB4_CV = 8;                      // float4 column vectors per workgroup
+constexpr int CMB4_PG = 32;                     // piece groups
+constexpr int CMB4_BATCH = 4;                   // pieces per thread per batch
+
+__global__ __launch_bounds__(256) void lse_combine_v4_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part, int32_t n_parts,
+                                                             int32_t D, void* out, int32_t out_bf16, float* lse_out) {
+    __shared__ float s_m[4], s_z[4];
+    __shared__ float4 s_acc[4][CMB4_CV];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cv = tid % CMB4_CV, pg = tid / CMB4_CV;
+    const int64_t row = blockIdx.x;
+    const int c4 = blockIdx.y * CMB4_CV + cv;
+    const bool col_ok = 4 * c4 < D;
+    const float* lrow = lse_part + row * n_parts;
+    const float* obase = o_part + row * (int64_t)n_parts * D + 4 * c4;
+    constexpr int PER_BATCH = CMB4_PG * CMB4_BATCH;
+
+    float lv[CMB4_BATCH];
+    float4 ov[CMB4_BATCH];
+    auto load_batch = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < CMB4_BATCH; ++u) {
+            const int i = base + pg + CMB4_PG * u;
+            lv[u] = (i < n_parts) ? lrow[i] : -INFINITY;
+            ov[u] = (i < n_parts && col_ok) ? *reinterpret_cast<const float4*>(obase + (int64_t)i * D)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    load_batch(0);
+
+    // Row maximum over all pieces.
+    float mloc = lv[0];
+#pragma unroll
+    for (int u = 1; u < CMB4_BATCH; ++u) mloc = fmaxf(mloc, lv[u]);
+    for (int i = PER_BATCH + pg; i < n_parts; i += CMB4_PG) mloc = fmaxf(mloc, lrow[i]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if (lane == 0) s_m[wave] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+
+    // This thread's weighted sums, batch by batch.
+    float z = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != -INFINITY) {
+        for (int base = 0;;) {
+#pragma unroll
+            for (int u = 0; u < CMB4_BATCH; ++u) {
+                const float w = (lv[u] == -INFINITY) ? 0.f : fast_exp2((lv[u] - M) * kLog2ef);
+                z += w;
+                a.x = fmaf(w, ov[u].x, a.x);
+                a.y = fmaf(w, ov[u].y, a.y);
+                a.z = fmaf(w, ov[u].z, a.z);
+                a.w = fmaf(w, ov[u].w, a.w);
+            }
+            base += PER_BATCH;
+            if (base >= n_parts) break;
+            load_batch(base);
+        }
+    }
+    // Sum over the wave's eight piece groups (lanes 8, 16, 32 apart), then
+    // over the waves.  Each column vector's lanes carry every piece, so
+    // their z is the wave's weight sum.
+#pragma unroll
+    for (int off = CMB4_CV; off < 64; off <<= 1) {
+        z += __shfl_xor(z, off);
+        a.x += __shfl_xor(a.x, off);
+        a.y += __shfl_xor(a.y, off);
+        a.z += __shfl_xor(a.z, off);
+        a.w += __shfl_xor(a.w, off);
+    }
+    if (lane < CMB4_CV) s_acc[wave][lane] = a;
+    if (lane == 0) s_z[wave] = z;
+    __syncthreads();
+    if (tid < CMB4_CV && col_ok) {
+        const float Z = (s_z[0] + s_z[1]) + (s_z[2] + s_z[3]);
+        float4 A = s_acc[0][tid];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            A.x += s_acc[w][tid].x;
+            A.y += s_acc[w][tid].y;
+            A.z += s_acc[w][tid].z;
+            A.w += s_acc[w][tid].w;
+        }
+        const float inv = (Z > 0.f) ? 1.f / Z : 0.f;
+        const int64_t o0 = row * D + 4 * c4;
+        store_out(out, o0, A.x * inv, out_bf16);
+        store_out(out, o0 + 1, A.y * inv, out_bf16);
+        store_out(out, o0 + 2, A.z * inv, out_bf16);
+        store_out(out, o0 + 3, A.w * inv, out_bf16);
+        if (c4 == 0 && lse_out) lse_out[row] = (Z > 0.f) ? M + logf(Z) : -INFINITY;
+    }
+}
+
 // LSE combine for rows with at most 64 pieces (the bifurcated calls and
 // short splits): one wave per row.  Lane j holds piece j's lse; the row
 // maximum and the weight sum are butterfly reductions (every lane ends with
@@ -680,8 +785,10 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                               int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
                               float* lse_out, hipStream_t stream) {
-    // One wave per row when rows are plentiful and pieces few; otherwise the
-    // column-slice kernel spreads a row over several workgroups.
+    // One wave per row when rows are plentiful and pieces few; otherwise a
+    // row spreads over several workgroups: 32 columns each with 16-byte
+    // loads, or 16 columns each (scalar loads) for other head dims or an
+    // unaligned o_part.
     if (n_parts <= 64 && rows >= 1024) {
         const dim3 grid((unsigned)((rows + CMBW_ROWS - 1) / CMBW_ROWS));
         const dim3 block(64 * CMBW_ROWS);
@@ -695,13 +802,15 @@ hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_
 #undef FD_CMBW
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
     const bool vec4 = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(o_part) % 16 == 0);
-    if (vec4)
-        hipLaunchKernelGGL(lse_combine_kernel<4>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
-                           n_parts, head_dim, out, out_bf16, lse_out);
-    else
-        hipLaunchKernelGGL(lse_combine_kernel<1>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
+    if (vec4) {
+        const dim3 grid4((unsigned)rows, (unsigned)((head_dim / 4 + CMB4_CV - 1) / CMB4_CV));
+        hipLaunchKernelGGL(lse_combine_v4_kernel, grid4, dim3(256), 0, stream, o_part, lse_part, n_parts, head_dim,
+                           out, out_bf16, lse_out);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
+    hipLaunchKernelGGL(lse_combine_kernel<1>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
                            n_parts, head_dim, out, out_bf16, lse_out);
     return hipGetLastError();
 }
