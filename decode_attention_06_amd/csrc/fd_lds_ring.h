@@ -20,11 +20,18 @@ constexpr int CTX_TILE_BYTES = CTX_TILE * 256;
 constexpr int XCDS = 8;
 
 // LDS byte offset of 16-byte chunk c (0..15) of token row t (0..31) in a
-// tile.  The chunk index is XORed with (t & 3) | (bits 3-4 of t) << 2, which
-// makes the K-operand reads (16 lanes: tokens {0..3, 8..11, 16..19, 24..27}
-// + const, one chunk) and the V-block reads (16 lanes: one token, chunks
-// 0..15) touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int t) { return (t & 3) | (((t >> 3) & 3) << 2); }
+// tile: the chunk index is XORed with a linear function of the row bits,
+// 2 t0 ^ 4 t1 ^ 8 t3 ^ 4 t4.  Bit 2 of the row never varies within one read
+// instruction (it is the token block of a K read, the half h of a V read).
+// The function was chosen against the bank behaviour measured with the
+// SQ_LDS_BANK_CONFLICT counter on gfx950: 64 four-byte banks; the
+// transposing 8-byte V reads serve 32 consecutive lanes per cycle, the
+// 16-byte K reads the 16 lanes of one residue mod 4.  With it neither read
+// conflicts (counter zero on the prefill kernel; the former XOR of
+// (t & 3) | (t >> 3 & 3) << 2 left every V read two cycles of conflicts).
+__device__ __forceinline__ int swz(int t) {
+    return ((t & 3) << 1) ^ (((t >> 3) & 1) << 3) ^ (((t >> 4) & 1) << 2);
+}
 __device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ swz(t)) << 4); }
 
 // Issue the loads of one 32-token tile straight into LDS
