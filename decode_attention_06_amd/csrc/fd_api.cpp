@@ -35,6 +35,8 @@ fd_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int32_t kWgPerCu = 2;        // partial-kernel workgroups to keep per CU
 constexpr int64_t kFewMfmaUnits = 8;   // at most this many units: one workgroup per CU
+constexpr int64_t kBalanceLen = 8192;  // several sequences at least this long (vector-ALU kernel):
+constexpr int64_t kBalancePieces = 4;  //   at least this many pieces each
 constexpr int64_t kMinChunk = 256;     // shortest piece worth a partial result (vector-ALU kernel)
 constexpr int64_t kMinChunkMfma = 128; // matrix-core kernel: one 32-token tile per wave
 constexpr int64_t kMaxLen = int64_t(1) << 30;
@@ -200,10 +202,14 @@ int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     // workgroup per CU, which halves the pieces to combine and reads as fast.
     const int64_t wg_per_cu = (path.mfma && units <= kFewMfmaUnits) ? 1 : kWgPerCu;
     const int64_t target = int64_t(n_cu) * wg_per_cu;
-    if (units >= target) return 1;
-    int64_t s = (target + units - 1) / units;
     const int64_t by_len = std::max<int64_t>(1, max_len / (path.mfma ? kMinChunkMfma * wg_per_cu : kMinChunk));
-    s = std::min<int64_t>(s, by_len);
+    int64_t s = (units >= target) ? 1 : std::min<int64_t>((target + units - 1) / units, by_len);
+    // Several sequences with long histories on the vector-ALU kernel: their
+    // lengths may differ (they are not known here), and one piece each
+    // would leave the longest to finish alone at the end; a few pieces each
+    // keep that tail short.
+    if (!path.mfma && batch > 1 && max_len >= kBalanceLen)
+        s = std::max<int64_t>(s, std::min<int64_t>(kBalancePieces, by_len));
     s = std::min<int64_t>(s, FD_MAX_SPLITS);
     return int32_t(std::max<int64_t>(s, 1));
 }

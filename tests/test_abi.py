@@ -56,9 +56,19 @@ def test_plan_invalid_arguments():
 
 
 def test_plan_full_gpu_needs_no_split():
-    # batch x heads already covers every CU twice over: one piece
-    assert fd.plan_splits(16, 32, 32, 128, 65536, fd.FD_BF16, 256) == 1
-    assert fd.plan_splits(64, 8, 8, 128, 1 << 20, fd.FD_BF16, 256) == 1
+    # batch x heads already covers every CU twice over: one piece, except
+    # for several long sequences on the vector-ALU kernel (next test)
+    assert fd.plan_splits(16, 32, 32, 128, 4096, fd.FD_BF16, 256) == 1
+    assert fd.plan_splits(256, 16, 2, 128, 1 << 20, fd.FD_BF16, 256) == 1     # matrix-core kernel
+
+
+def test_plan_balances_several_long_sequences():
+    # lengths of several sequences may differ: long ones get four pieces each
+    assert fd.plan_splits(16, 32, 32, 128, 65536, fd.FD_BF16, 256) == 4
+    assert fd.plan_splits(64, 8, 8, 128, 1 << 20, fd.FD_BF16, 256) == 4
+    assert fd.plan_splits(16, 32, 32, 128, 8192, fd.FD_BF16, 256) == 4
+    assert fd.plan_splits(16, 32, 32, 128, 2048, fd.FD_BF16, 256) == 1       # short: the combine costs more
+    assert fd.plan_splits(1, 32, 32, 128, 65536, fd.FD_BF16, 256) == 16      # one sequence: by CU count
 
 
 def test_plan_long_single_sequence_splits_a_lot():
