@@ -653,7 +653,9 @@ __global__ __launch_bounds__(256) void lse_combine_v4_kernel(const float* __rest
 // short splits): one wave per row.  Lane j holds piece j's lse; the row
 // maximum and the weight sum are butterfly reductions (every lane ends with
 // the same bits); piece weights reach all lanes through v_readlane, and lane
-// j accumulates columns j, j + 64, ... with up to 8 pieces' loads in flight.
+// j accumulates columns j, j + 64, ...  The first batch of pieces (32 for
+// head dims up to 128) is requested together with the lse values, so a row
+// of up to that many pieces costs one memory round trip.
 constexpr int CMBW_ROWS = 4;                    // rows (waves) per workgroup
 constexpr int CMBW_MAXV = 8;                    // columns per lane: D <= 512
 
@@ -663,10 +665,25 @@ __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const 
                                                                           int32_t rows, int32_t n_parts, int32_t D,
                                                                           void* out, int32_t out_bf16,
                                                                           float* lse_out) {
+    constexpr int PB = NV <= 2 ? 32 : (NV <= 4 ? 16 : 8);   // pieces per batch (64 loads in flight)
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * CMBW_ROWS + (threadIdx.x >> 6);
     if (row >= rows) return;
+    const float* base = o_part + row * (int64_t)n_parts * D;
+    float v[PB][NV];
+    auto load = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int i = min(i0 + u, n_parts - 1);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int d = lane + 64 * k;
+                v[u][k] = (d < D) ? base[(int64_t)i * D + d] : 0.f;
+            }
+        }
+    };
     const float li = (lane < n_parts) ? lse_part[row * n_parts + lane] : -INFINITY;
+    load(0);
     float M = li;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -675,29 +692,21 @@ __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const 
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
 
-    const float* base = o_part + row * (int64_t)n_parts * D;
     float acc[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) acc[k] = 0.f;
-    for (int i0 = 0; i0 < n_parts; i0 += 8) {
-        float v[8][NV];
+    for (int i0 = 0;;) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = min(i0 + u, n_parts - 1);
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int d = lane + 64 * k;
-                v[u][k] = (d < D) ? base[(int64_t)i * D + d] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < PB; ++u) {
             if (i0 + u < n_parts) {
                 const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i0 + u));
 #pragma unroll
                 for (int k = 0; k < NV; ++k) acc[k] = fmaf(wf, v[u][k], acc[k]);
             }
         }
+        i0 += PB;
+        if (i0 >= n_parts) break;
+        load(i0);
     }
     const float inv = (Z > 0.f) ? 1.f / Z : 0.f;
 #pragma unroll
