@@ -11,12 +11,12 @@
 // decodificación necesita otra planificación") whose partial outputs and
 // log-sum-exps join the decode pieces in the LSE combine.
 //
-// Work unit: (KV head, context piece, tile of 32 * NW query rows, NW = 4
-// or 8 waves).  The
-// query rows of a KV head are the (sample, head-in-group) pairs that read it,
-// S * G of them.  A workgroup streams 32-token K/V tiles straight from global
-// memory into a ring of LDS stages (XOR-swizzled 16-byte chunks, three tiles
-// in flight) and every wave contracts them
+// Work unit: (KV head, context piece, tile of 128 query rows over four
+// waves).  The query rows of a KV head are the (sample, head-in-group)
+// pairs that read it, S * G of them.  A workgroup streams 32-token K/V
+// tiles straight from global memory into a ring of LDS stages (16-byte
+// chunks permuted against bank conflicts, three tiles in flight) and every
+// wave contracts them
 // against its own 32 rows with the same register layout as the split-KV
 // matrix-core kernel, so each wave owns its rows for the whole piece and no
 // cross-wave merge is needed.  Workgroup ids are arranged so that all row

@@ -120,7 +120,7 @@ __device__ __forceinline__ PagedTile paged_tile(const PartialParams& p, int b, i
 }
 
 // NRB blocks of 16 query rows per work unit share every K/V load; NW waves
-// per workgroup take interleaved 32-token tiles of the unit's piece.  The
+// per workgroup take turns at the 32-token tiles of the unit's piece.  The
 // waves' states meet in LDS: per-row max and sum first, then each wave's
 // accumulators already scaled by its weight in the merged sum, at word
 // row * MF_ACC_STRIDE + d.  Lane (g, i) stores d = 32g + 8ii + e0 .. +3 as
