@@ -203,14 +203,20 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     }
 
     // Paged: first rows and page ids of the 16-row groups of the next tile
-    // to load (scalar loads, issued one tile ahead of their use).
-    int gs[NG], gid[NG];
-    auto lookup = [&](int at) {
+    // to load (gs, gid) and of the one after (gs2, gid2): scalar loads issued
+    // two tile loads ahead of their use, so the first two loads wait for one
+    // round trip.
+    int gs[NG], gid[NG], gs2[NG], gid2[NG];
+    auto lookup = [&](int at, int (&s_out)[NG], int (&id_out)[NG]) {
 #pragma unroll
         for (int h = 0; h < NG; ++h) {
-            gs[h] = kv_group_start(at + 16 * h, t1 - 1);
-            gid[h] = kv_page_id(p, b, gs[h]);
+            s_out[h] = kv_group_start(at + 16 * h, t1 - 1);
+            id_out[h] = kv_page_id(p, b, s_out[h]);
         }
+    };
+    auto lookup_first = [&](int at) {
+        lookup(at, gs, gid);
+        lookup(at + wg_step, gs2, gid2);
     };
 
     // Loads one wave tile starting at row tb.  Unconditional: rows at or
@@ -236,7 +242,14 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
             kr[u] = *reinterpret_cast<const uint4*>(kpool + gb[h] + off);
             vr[u] = *reinterpret_cast<const uint4*>(vpool + gb[h] + off);
         }
-        if constexpr (PAGED) lookup(tb + wg_step);
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                gs[h] = gs2[h];
+                gid[h] = gid2[h];
+            }
+            lookup(tb + 2 * wg_step, gs2, gid2);
+        }
     };
 
     // Scores, online-softmax update and P.V for one loaded wave tile.
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     const int tb0 = t0 + wave * WAVE_TOK;
     if (GB >= 8) {
         if (tb0 < t1) {
-            if constexpr (PAGED) lookup(tb0);
+            if constexpr (PAGED) lookup_first(tb0);
             uint4 ka[U], va[U];
             for (int tb = tb0; tb < t1; tb += wg_step) {
                 load(tb, ka, va);
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     } else if (tb0 < t1) {
         const int ntiles = (t1 - tb0 + wg_step - 1) / wg_step;
         uint4 ka[U], va[U], kn[U], vn[U];
-        if constexpr (PAGED) lookup(tb0);
+        if constexpr (PAGED) lookup_first(tb0);
         load(tb0, ka, va);
         load(tb0 + wg_step, kn, vn);
         int tb = tb0;

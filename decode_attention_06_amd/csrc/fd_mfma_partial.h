@@ -223,8 +223,10 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // every path leaves the same number of loads outstanding and the wait
     // before each tile covers only that tile's own loads.
     Tile ta, tn;
-    // Paged: `ahead` holds the page ids of the next tile to load.
-    PagedTile ahead{};
+    // Paged: `ahead` holds the page ids of the next tile to load and
+    // `ahead2` those of the one after: each lookup is issued two loads
+    // before its use, so the prologue's two loads wait for one round trip.
+    PagedTile ahead{}, ahead2{};
     auto load = [&](int at, Tile& r) {
         if constexpr (PAGED) {
             // Offsets to row 0 of each group's page (row t of the group
@@ -232,14 +234,18 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
             const int64_t o0 = kv_page_offset<MF_D>(p, ahead.id0, kvh, ahead.s0) - (int64_t)ahead.s0 * MF_D;
             const int64_t o1 = kv_page_offset<MF_D>(p, ahead.id1, kvh, ahead.s1) - (int64_t)ahead.s1 * MF_D;
             load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, at, t1 - 1, ktok0, g, i, r);
-            ahead = paged_tile(p, b, at + step, t1 - 1);
+            ahead = ahead2;
+            ahead2 = paged_tile(p, b, at + 2 * step, t1 - 1);
         } else {
             load_rows(kpool, vpool, slice, slice, at, t1 - 1, ktok0, g, i, r);
         }
     };
     int tb = t0 + wave * MF_TILE;
     if (tb < t1) {
-        if constexpr (PAGED) ahead = paged_tile(p, b, tb, t1 - 1);
+        if constexpr (PAGED) {
+            ahead = paged_tile(p, b, tb, t1 - 1);
+            ahead2 = paged_tile(p, b, tb + step, t1 - 1);
+        }
         load(tb, ta);
         while (true) {
             load(tb + step, tn);
