@@ -118,9 +118,13 @@ def test_bitwise_repeatable(fd):
 # ------------------------------------------------------------ combine op
 
 @pytest.mark.parametrize("rows,P,D", [(37, 19, 128), (5, 64, 128), (9, 65, 128), (4, 300, 128), (7, 3, 64),
-                                      (6, 40, 100), (3, 70, 100), (2, 1, 128), (3, 17, 512)])
+                                      (6, 40, 100), (3, 70, 100), (2, 1, 128), (3, 17, 512),
+                                      (1100, 40, 128), (1024, 64, 64), (1030, 17, 512), (1024, 33, 256),
+                                      (1025, 1, 128)])
 def test_lse_combine_matches_oracle(fd, rows, P, D):
-    # up to 64 pieces: one wave per row; more: the column-slice kernel
+    # >= 1024 rows with <= 64 pieces: one wave per row (batches of 32, 16 or
+    # 8 pieces by head dim, so 33..64 pieces take a second batch); otherwise
+    # the column-slice kernels
     rng = np.random.Generator(np.random.PCG64(12 + P))
     o = rng.standard_normal((rows, P, D)).astype(np.float32)
     lse = (rng.standard_normal((rows, P)) * 5).astype(np.float32)
