@@ -34,7 +34,6 @@
 namespace fd {
 namespace {
 
-
 // Context role: one work unit (KV head, piece, row tile) given by bid.
 template <int NW>
 __device__ __forceinline__ void context_body(const BifContextParams& p, int bid, char* lds) {

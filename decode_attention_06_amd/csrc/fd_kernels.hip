@@ -239,8 +239,8 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
             const int h = (NG > 1) ? (u * RPW) / 16 : 0;
             const int t = min(tb + u * RPW + r, t1 - 1);
             const uint32_t off = (uint32_t)(t - gs[h]) * (uint32_t)(D * SZ) + lane_off;
-            kr[u] = *reinterpret_cast<const uint4*>(kpool + gb[h] + off);
-            vr[u] = *reinterpret_cast<const uint4*>(vpool + gb[h] + off);
+            kr[u] = ld_stream16(kpool + gb[h] + off);
+            vr[u] = ld_stream16(vpool + gb[h] + off);
         }
         if constexpr (PAGED) {
 #pragma unroll
@@ -731,8 +731,9 @@ __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const 
 }
 
 // HBM read ceiling: each workgroup streams one contiguous chunk of the
-// buffer with 16-byte loads, eight in flight per thread, and folds the data
-// into a word so the loads cannot be dropped.
+// buffer with 16-byte loads (the KV loads' non-temporal hint), eight in
+// flight per thread, and folds the data into a word so the loads cannot be
+// dropped.
 constexpr int PROBE_UNROLL = 8;
 constexpr size_t PROBE_CHUNK = 16384;          // bytes per workgroup
 
@@ -747,7 +748,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 #pragma unroll
         for (int u = 0; u < PROBE_UNROLL; ++u) {
             const size_t j = min(i + (size_t)u * 256, end - 1);
-            v[u] = buf[j];
+            v[u] = ld_stream16(buf + j);
         }
 #pragma unroll
         for (int u = 0; u < PROBE_UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;

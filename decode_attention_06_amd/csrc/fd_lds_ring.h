@@ -41,6 +41,11 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ sw
 // writes row 8w + 4k + L/16 at chunk position L%16, so it fetches chunk
 // (L%16) ^ swz(row) of that row.  Rows at or beyond c1 clamp to c1 - 1
 // (c1 > t0 is not required: a tile past the end re-reads row c1 - 1).
+// The loads keep the default cache policy, unlike the split-KV kernels'
+// read-once KV loads: several workgroups read each tile (the row tiles of a
+// bifurcated context piece, every later position tile in prefill), and the
+// non-temporal hint measured slower on both (bifurcated 1-3%, prefill
+// 2-11%).
 // Addresses are a wave-uniform base (row min(t0, c1 - 1)) plus a 32-bit
 // lane offset below 8 KiB, shared by K and V.  Four vector-memory
 // instructions per wave.

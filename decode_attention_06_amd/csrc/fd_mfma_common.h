@@ -27,8 +27,17 @@ constexpr int MF_NW = 4;      // waves per workgroup (split-KV kernel)
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
-__device__ __forceinline__ u32x4_t ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-__device__ __forceinline__ u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
+// KV cache loads with the non-temporal hint (see ld_stream16).
+__device__ __forceinline__ u32x4_t ld16_kv(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x4_t ld16_kv(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t ld8_kv(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 

@@ -48,12 +48,12 @@ __device__ __forceinline__ void load_rows(const uint16_t* kpool, const uint16_t*
         const int t = min(tb + ktok0 + 4 * blk, last);
         const uint16_t* src = kpool + ko + (int64_t)t * MF_D + 8 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16(src + 32 * s);
+        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16_kv(src + 32 * s);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = min(tb + 8 * g + j, last);
-        r.v[j] = ld16(vpool + vo + (int64_t)t * MF_D + 8 * i);
+        r.v[j] = ld16_kv(vpool + vo + (int64_t)t * MF_D + 8 * i);
     }
 }
 
@@ -63,13 +63,13 @@ __device__ __forceinline__ void load_rows(const uint8_t* kpool, const uint8_t* v
     for (int blk = 0; blk < 2; ++blk) {
         const int t = min(tb + ktok0 + 4 * blk, last);
         const uint8_t* src = kpool + ko + (int64_t)t * MF_D + 32 * g;
-        r.k[blk][0] = ld16(src);
-        r.k[blk][1] = ld16(src + 16);
+        r.k[blk][0] = ld16_kv(src);
+        r.k[blk][1] = ld16_kv(src + 16);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = min(tb + 8 * g + j, last);
-        r.v[j] = ld8(vpool + vo + (int64_t)t * MF_D + 8 * i);
+        r.v[j] = ld8_kv(vpool + vo + (int64_t)t * MF_D + 8 * i);
     }
 }
 
