@@ -77,9 +77,16 @@ def test_plan_long_single_sequence_splits_a_lot():
 
 
 def test_plan_short_history_limits_splitting():
-    # pieces are never planned shorter than the minimum chunk
-    assert fd.plan_splits(1, 32, 32, 128, 512, fd.FD_BF16, 256) <= 2
+    # pieces are never planned shorter than one workgroup step of the
+    # kernel's rows (vector-ALU kernel: 128 rows for bf16 at D 128, fp32 at
+    # D 64 and E4M3 with up to two query rows per unit; 64 with more)
+    assert fd.plan_splits(1, 32, 32, 128, 512, fd.FD_BF16, 256) == 4
+    assert fd.plan_splits(1, 32, 32, 128, 2048, fd.FD_BF16, 256) == 16
+    assert fd.plan_splits(1, 4, 4, 64, 512, fd.FD_F32, 256) == 4
+    assert fd.plan_splits(1, 8, 2, 64, 512, fd.FD_F32, 256) == 8        # 4 query rows per unit: 64-row steps
     assert fd.plan_splits(1, 4, 4, 64, 100, fd.FD_F32, 256) == 1
+    assert fd.plan_splits(1, 4, 4, 64, 127, fd.FD_F32, 256) == 1
+    assert fd.plan_splits(1, 4, 4, 64, 256, fd.FD_F32, 256) == 2
 
 
 @pytest.mark.parametrize("L", [512, 2048, 8192, 32768, 65536, 1 << 20])
