@@ -328,7 +328,8 @@ fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t row
 /*
  * fd_read_probe - measurement aid, not part of the attention path: streams
  * `bytes` (a positive multiple of 16, buf 16-byte aligned) once with the
- * 16-byte coalesced loads the partial kernels use and folds them into one
+ * 16-byte coalesced loads the partial kernels use (non-temporal hint
+ * included) and folds them into one
  * word (sink, 4 bytes of device memory, is written only in a
  * data-dependent corner case).  Timing it gives the HBM read rate this
  * device actually sustains, the ceiling for the KV stream.
