@@ -466,7 +466,8 @@ def main():
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "(a longer history would be split over GPUs with fd_decode_attn_partials and merged with "
+              "fd_lse_combine after an all-gather); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch

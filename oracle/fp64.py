@@ -28,7 +28,7 @@ Sources (the pages this follows; cited by title and section):
   result is exact and the FLOPs are unchanged.  Section "Tilastot": KV-cache
   IO is b*g*m*k for multi-query versus b*h*m*k for multi-head attention.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * scale defaults to 1/sqrt(D);
 * query head h reads KV head h // (Hq // Hkv) (contiguous GQA groups);
