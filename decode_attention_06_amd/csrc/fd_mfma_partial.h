@@ -101,8 +101,8 @@ __device__ __forceinline__ void compute_loaded(const Fp8Tile& r, const bf16x8_t 
 
 // Paged tiles.  A tile (16-row aligned) covers two 16-row groups, each
 // inside one page: PagedTile holds their first rows and page ids (wave-
-// uniform; the ids come from scalar loads, looked up one tile ahead so that
-// their latency hides behind the current tile's work).  A lane's K rows lie
+// uniform; the ids come from scalar loads, looked up two tile loads ahead
+// so that their latency hides behind the tiles in between).  A lane's K rows lie
 // in group i / 8 and its V rows in group g / 2; rows at or beyond t1 clamp
 // to t1 - 1, and kv_group_start gives the group that then holds them.
 struct PagedTile {
