@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libf
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
 FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
 FD_MAX_SPLITS = 4096
+FD_NOALLOC_MAX_WORKSPACE = 16 << 20
 FD_PIECES_CONTIGUOUS, FD_PIECES_INTERLEAVED = 0, 1
 
 # Exported symbols and their ctypes signatures (mirrors include/fd.h).
@@ -29,6 +30,8 @@ SIGNATURES = {
                                                ctypes.POINTER(_c_sz)]),
     "fd_decode_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                 _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "fd_decode_attn_noalloc": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                        _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp]),
     "fd_decode_attn_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i64, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp]),
     "fd_decode_attn_paged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -169,6 +172,34 @@ def decode_attn(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=
                               B, Hq, Hkv, D, Lmax, dt, int(n_splits), _dev_ptr(out, "out"), _dtype_code(out),
                               _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def decode_attn_noalloc(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=0.0,
+                        return_lse=False, stream=None):
+    """fd_decode_attn_noalloc: decode_attn with the partials in the library's
+    fixed per-GPU array (no workspace); calls on one GPU must not overlap."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise FdError(FD_ERR_INVALID_ARG, "expected q [B,Hq,D] and k, v [B,Hkv,Lmax,D]")
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, Dk = k.shape
+    if k.shape[0] != B or Dk != D:
+        raise FdError(FD_ERR_INVALID_ARG, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise FdError(FD_ERR_UNSUPPORTED, "q, k and v must share one dtype")
+    if lens is not None and (lens.dtype != torch.int32 or lens.shape != (B,)):
+        raise FdError(FD_ERR_INVALID_ARG, "lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise FdError(FD_ERR_INVALID_ARG, "out must be [B, Hq, D]")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.fd_decode_attn_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _opt_ptr(lens, "lens"),
+                                      B, Hq, Hkv, D, Lmax, dt, int(n_splits), _dev_ptr(out, "out"),
+                                      _dtype_code(out), _opt_ptr(lse, "lse"), float(scale), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

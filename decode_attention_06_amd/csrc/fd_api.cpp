@@ -172,6 +172,14 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
 
 }  // namespace
 
+fd_status fd::set_error(fd_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
 extern "C" {
 
 const char* fd_status_string(fd_status s) {

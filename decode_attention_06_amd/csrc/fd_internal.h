@@ -5,7 +5,13 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "fd.h"
+
 namespace fd {
+
+// Records the thread-local text fd_last_error_message() returns and passes
+// the status through (printf-style format).
+fd_status set_error(fd_status s, const char* fmt, ...);
 
 // Most pieces one combine can merge per output row (LDS holds their weights).
 #define FD_MAX_PARTS 4096

@@ -174,6 +174,30 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
                          int32_t n_splits, void* out, int32_t out_dtype, float* lse_out,
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of partials fd_decode_attn_noalloc can hold (16 MiB): that many per
+ * GPU stay reserved inside the library until the process ends. */
+#define FD_NOALLOC_MAX_WORKSPACE (16u << 20)
+
+/*
+ * fd_decode_attn_noalloc - fd_decode_attn for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  It calls no allocating routine of any kind.
+ *
+ * Arguments, results and errors are those of fd_decode_attn without the
+ * workspace: the partials live in a fixed array of FD_NOALLOC_MAX_WORKSPACE
+ * bytes inside the library, one per GPU, held until the process ends.  A
+ * call whose partials need more (fd_decode_attn_workspace_size with the
+ * same shapes and split count) returns FD_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  The first call on each device
+ * looks up that device's copy of the array (hipGetSymbolAddress).
+ */
+fd_status fd_decode_attn_noalloc(const void* q, const void* k, const void* v, const int32_t* lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int64_t max_len, int32_t dtype, int32_t n_splits,
+                                 void* out, int32_t out_dtype, float* lse_out, float scale, void* stream);
+
 /*
  * fd_decode_attn_fp8 - fd_decode_attn over a KV cache of 8-bit floating
  * point codes ([MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", quantisation

@@ -317,3 +317,17 @@ def test_partials_reject_unknown_piece_layout(lib):
                                          FAKE, 0.0, None)
         assert st == fd.FD_ERR_INVALID_ARG
         assert "piece_layout" in lib.fd_last_error_message().decode()
+
+
+def test_noalloc_checks_before_any_hip_call(lib):
+    def call(q=FAKE, B=1, n_splits=4, L=512):
+        return lib.fd_decode_attn_noalloc(q, FAKE, FAKE, None, B, 4, 4, 64, L, fd.FD_F32, n_splits, FAKE,
+                                          fd.FD_F32, None, 0.0, None)
+    # partials beyond the fixed array: 1024 x 32 rows x 256 pieces x 65 floats
+    assert lib.fd_decode_attn_noalloc(FAKE, FAKE, FAKE, None, 1024, 32, 32, 64, 4096, fd.FD_F32, 256, FAKE,
+                                      fd.FD_F32, None, 0.0, None) == fd.FD_ERR_WORKSPACE
+    assert "16777216" in lib.fd_last_error_message().decode()
+    assert call(q=None) == fd.FD_ERR_INVALID_ARG
+    assert call(q=MISALIGNED) == fd.FD_ERR_INVALID_ARG
+    assert call(B=0) == fd.FD_ERR_INVALID_ARG
+    assert call(n_splits=fd.FD_MAX_SPLITS + 1) == fd.FD_ERR_INVALID_ARG
