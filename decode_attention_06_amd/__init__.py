@@ -10,13 +10,17 @@ built the first call raises: there is no fallback implementation.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfd.so")
+# FD_LIBRARY_PATH names another build of the same library (the sanitized
+# build the CPU tests run under AddressSanitizer); default: the in-tree one.
+LIB_PATH = os.environ.get("FD_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                             "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
 FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
 FD_MAX_SPLITS = 4096
 FD_NOALLOC_MAX_WORKSPACE = 16 << 20
 FD_PIECES_CONTIGUOUS, FD_PIECES_INTERLEAVED = 0, 1
+TESTING_KERNELS = {"auto": 0, "valu": 1, "mfma": 2}   # include/fd_testing.h
 
 # Exported symbols and their ctypes signatures (mirrors include/fd.h).
 _c_i32, _c_i64, _c_sz, _c_vp, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -48,7 +52,31 @@ SIGNATURES = {
     "fd_decode_attn_partials": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                          _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_f32, _c_vp]),
     "fd_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_vp]),
+    "fd_testing_decode_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_i64, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32, _c_vp, _c_sz, _c_vp,
+                                        _c_i32]),
 }
+
+
+
+class FdTensor(ctypes.Structure):
+    """fd_tensor (include/fd.h): device pointer, fd_dtype, ndim, shape[4], stride[4] (elements)."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+_P_T = ctypes.POINTER(FdTensor)
+SIGNATURES.update({
+    "fd_set_validation": (_c_i32, [_c_i32]),
+    "fd_validation_enabled": (_c_i32, []),
+    "fd_decode_attn_strided": (_c_i32, [_P_T, _P_T, _P_T, _c_vp, _c_vp, _c_vp, _c_i32, _P_T, _c_vp, _c_f32, _c_vp,
+                                        _c_sz, _c_vp]),
+    "fd_bifurcated_attn_strided": (_c_i32, [_P_T, _P_T, _P_T, _P_T, _P_T, _c_vp, _P_T, _c_vp, _c_f32, _c_vp, _c_sz,
+                                            _c_vp]),
+    "fd_bifurcated_attn_paged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                          _c_i32, _c_i64, _c_i32, _c_i64, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_f32,
+                                          _c_vp, _c_sz, _c_vp]),
+})
 
 _lib = None
 
@@ -405,6 +433,139 @@ def decode_attn_partials(q, k, v, n_splits, lens=None, o_part=None, lse_part=Non
                                        int(layout), _dev_ptr(o_part, "o_part"), _dev_ptr(lse_part, "lse_part"),
                                        float(scale), _stream(stream)))
     return o_part, lse_part
+
+
+def testing_decode_attn(q, k, v, kernel, k_scale=None, v_scale=None, lens=None, n_splits=0, out=None,
+                        out_dtype=None, scale=0.0, return_lse=False, stream=None):
+    """fd_testing_decode_attn (test hook): decode attention on the named
+    partial kernel ('auto', 'valu' or 'mfma').  k, v are bf16/fp32 like q,
+    or E4M3 codes (uint8 / float8_e4m3fn) with a bf16 q and optional scales."""
+    torch = _torch()
+    lib = load()
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k.shape
+    fp8 = k.dtype in (torch.uint8, torch.float8_e4m3fn)
+    dt = FD_FP8_E4M3 if fp8 else _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = decode_workspace_size(B, Hq, Hkv, D, Lmax, dt, n_splits)
+    workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    kp = _fp8_codes(k, "k") if fp8 else _dev_ptr(k, "k")
+    vp = _fp8_codes(v, "v") if fp8 else _dev_ptr(v, "v")
+    _check(lib.fd_testing_decode_attn(_dev_ptr(q, "q"), kp, vp, _opt_ptr(k_scale, "k_scale"),
+                                      _opt_ptr(v_scale, "v_scale"), _opt_ptr(lens, "lens"), B, Hq, Hkv, D, Lmax, dt,
+                                      int(n_splits), _dev_ptr(out, "out"), _dtype_code(out), _opt_ptr(lse, "lse"),
+                                      float(scale), _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                      _stream(stream), TESTING_KERNELS[kernel]))
+    return (out, lse) if return_lse else out
+
+
+def _tensor_desc(t, name, dtype=None):
+    """fd_tensor describing a device tensor of any strides (no copy)."""
+    if not t.is_cuda:
+        raise FdError(FD_ERR_INVALID_ARG, f"{name} must be a device tensor")
+    d = FdTensor()
+    d.data = t.data_ptr()
+    d.dtype = _dtype_code(t) if dtype is None else dtype
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def decode_attn_strided(q, k, v, lens=None, n_splits=0, out=None, out_dtype=None, scale=0.0, k_scale=None,
+                        v_scale=None, return_lse=False, workspace=None, stream=None):
+    """fd_decode_attn_strided: q [B, Hq, D], k, v logical [B, Hkv, Lmax, D] and
+    out [B, Hq, D] as views of any strides (last dimension contiguous), e.g.
+    a token-major cache passed as kt.permute(0, 2, 1, 3).  k, v may be E4M3
+    codes (uint8 / float8_e4m3fn) with a bf16 q and optional scales."""
+    torch = _torch()
+    lib = load()
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k.shape
+    fp8 = k.dtype in (torch.uint8, torch.float8_e4m3fn)
+    dt = FD_FP8_E4M3 if fp8 else _dtype_code(k)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = decode_workspace_size(B, Hq, Hkv, D, Lmax, dt, n_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    qd, kd, vd, od = (_tensor_desc(q, "q"), _tensor_desc(k, "k", dt), _tensor_desc(v, "v", dt),
+                      _tensor_desc(out, "out"))
+    _check(lib.fd_decode_attn_strided(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                                      _opt_ptr(k_scale, "k_scale"), _opt_ptr(v_scale, "v_scale"),
+                                      _opt_ptr(lens, "lens"), int(n_splits), ctypes.byref(od), _opt_ptr(lse, "lse"),
+                                      float(scale), _dev_ptr(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def bifurcated_attn_strided(q, k_ctx, v_ctx, k_dec, v_dec, dec_lens=None, out=None, out_dtype=None, scale=0.0,
+                            return_lse=False, workspace=None, stream=None):
+    """fd_bifurcated_attn_strided: q [S, Hq, D], k_ctx, v_ctx logical [Hkv, Lc, D],
+    k_dec, v_dec logical [S, Hkv, Ldmax, D], out [S, Hq, D], as views of any
+    strides (last dimension contiguous)."""
+    torch = _torch()
+    lib = load()
+    S, Hq, D = q.shape
+    Hkv, Lc, _ = k_ctx.shape
+    Ld = k_dec.shape[2]
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = bifurcated_workspace_size(S, Hq, Hkv, D, Lc, Ld, _dtype_code(q))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    descs = [_tensor_desc(t, n) for t, n in ((q, "q"), (k_ctx, "k_ctx"), (v_ctx, "v_ctx"), (k_dec, "k_dec"),
+                                              (v_dec, "v_dec"), (out, "out"))]
+    qd, kcd, vcd, kdd, vdd, od = descs
+    _check(lib.fd_bifurcated_attn_strided(ctypes.byref(qd), ctypes.byref(kcd), ctypes.byref(vcd), ctypes.byref(kdd),
+                                          ctypes.byref(vdd), _opt_ptr(dec_lens, "dec_lens"), ctypes.byref(od),
+                                          _opt_ptr(lse, "lse"), float(scale), _dev_ptr(workspace, "workspace"),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def bifurcated_attn_paged(q, k_ctx, v_ctx, k_pages, v_pages, block_table, dec_lens=None, out=None, out_dtype=None,
+                          scale=0.0, return_lse=False, workspace=None, stream=None):
+    """fd_bifurcated_attn_paged: q [S, Hq, D]; k_ctx, v_ctx [Hkv, Lc, D] dense;
+    the decode rows in k_pages, v_pages [num_pages, Hkv, page_size, D] found
+    through block_table int32 [S, max_pages_per_seq]; dec_lens int32 [S]."""
+    torch = _torch()
+    lib = load()
+    S, Hq, D = q.shape
+    Hkv, Lc, _ = k_ctx.shape
+    n_pages, _, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    if block_table.dtype != torch.int32 or tuple(block_table.shape[:1]) != (S,):
+        raise FdError(FD_ERR_INVALID_ARG, "block_table must be int32 [S, max_pages_per_seq]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        nbytes = bifurcated_workspace_size(S, Hq, Hkv, D, Lc, max_pages * page_size, dt)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fd_bifurcated_attn_paged(_dev_ptr(q, "q"), _dev_ptr(k_ctx, "k_ctx"), _dev_ptr(v_ctx, "v_ctx"),
+                                        _dev_ptr(k_pages, "k_pages"), _dev_ptr(v_pages, "v_pages"),
+                                        _dev_ptr(block_table, "block_table"), _opt_ptr(dec_lens, "dec_lens"), S, Hq,
+                                        Hkv, D, Lc, page_size, n_pages, max_pages, dt, _dev_ptr(out, "out"),
+                                        _dtype_code(out), _opt_ptr(lse, "lse"), float(scale),
+                                        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def set_validation(on):
+    """fd_set_validation: device-side checks of lens / block tables before each call."""
+    _check(load().fd_set_validation(1 if on else 0))
+
+
+def validation_enabled():
+    return bool(load().fd_validation_enabled())
 
 
 def read_probe(buf, sink, stream=None):

@@ -3,6 +3,7 @@
 // before the first HIP call; no entry point allocates device memory or
 // synchronises a stream.
 #include "fd.h"
+#include "fd_testing.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -10,9 +11,9 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
-#include <cstring>
+#include <algorithm>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "fd_internal.h"
@@ -40,6 +41,7 @@ constexpr int64_t kBalancePieces = 4;  //   at least this many pieces each
 constexpr int64_t kMinChunk = 256;     // shortest vector-ALU piece where no kernel step applies
 constexpr int64_t kMinChunkMfma = 128; // matrix-core kernel: one 32-token tile per wave
 constexpr int64_t kMaxLen = int64_t(1) << 30;
+constexpr int64_t kMaxUnits = int64_t(1) << 30;   // workgroups or output rows of one launch
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -100,23 +102,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMfmaMinGroup = 4;
 
 // Which partial kernel serves a (dtype, D, G) call, and how many query-row
-// blocks each KV head is cut into.  FD_PARTIAL_KERNEL=valu|mfma overrides
-// the choice where both kernels support the shape (used to compare them).
+// blocks each KV head is cut into.  The choice depends on the shapes only;
+// `force` (the test entry point fd_testing_decode_attn alone passes it)
+// picks a kernel where both support the shape.
 struct Path {
     bool mfma;
     int rows_per_block;
     int row_blocks;
 };
 
-Path choose_path(int32_t dtype, int32_t D, int G) {
-    const bool mfma_ok = (dtype == FD_BF16 || dtype == FD_FP8_E4M3) && D == 128;
-    bool mfma = mfma_ok && G >= kMfmaMinGroup;
-    if (mfma_ok) {
-        if (const char* env = std::getenv("FD_PARTIAL_KERNEL")) {
-            if (!std::strcmp(env, "valu")) mfma = false;
-            if (!std::strcmp(env, "mfma")) mfma = true;
-        }
-    }
+bool mfma_supported(int32_t dtype, int32_t D) { return (dtype == FD_BF16 || dtype == FD_FP8_E4M3) && D == 128; }
+
+Path choose_path(int32_t dtype, int32_t D, int G, int32_t force = FD_TESTING_KERNEL_AUTO) {
+    bool mfma = mfma_supported(dtype, D) && G >= kMfmaMinGroup;
+    if (force == FD_TESTING_KERNEL_VALU) mfma = false;
+    if (force == FD_TESTING_KERNEL_MFMA) mfma = true;
     Path path;
     path.mfma = mfma;
     path.rows_per_block = mfma ? fd::mfma_rows_per_block(G) : fd::valu_rows_per_block(G, dtype == FD_FP8_E4M3);
@@ -168,6 +168,82 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
         b.pd = fd_plan_splits(S, Hq, Hkv, D, Ld, dtype, n_cu);
     }
     return b;
+}
+
+// Element strides of the query and output tensors [B, Hq, D] (D
+// contiguous).  The KV cache's strides travel in PartialParams.
+struct IoStrides {
+    int64_t q_b, q_h;
+    int64_t out_b, out_h;
+};
+
+IoStrides dense_io(int32_t Hq, int32_t D) { return {int64_t(Hq) * D, D, int64_t(Hq) * D, D}; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == FD_F32 ? 4 : dtype == FD_BF16 ? 2 : 1; }
+
+// Rows of one KV head are read with 32-bit offsets inside 16- and 32-row
+// groups, formed by 24-bit multiplies: a row stride below 2^24 elements and
+// 2^27 bytes keeps them exact.
+constexpr int64_t kMaxRowStride = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxRowStrideBytes = int64_t(1) << 27;
+
+// One fd_tensor argument: present, ndim dimensions of positive extent, the
+// last contiguous, every other stride non-negative and a multiple of 16
+// bytes (the kernels read 16-byte vectors), data 16-byte aligned.
+fd_status check_tensor(const fd_tensor* t, int32_t ndim, const char* name) {
+    if (!t) return fail(FD_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+    if (t->ndim != ndim) return fail(FD_ERR_INVALID_ARG, "%s has %d dimensions, %d expected", name, t->ndim, ndim);
+    if (t->dtype != FD_F32 && t->dtype != FD_BF16 && t->dtype != FD_FP8_E4M3)
+        return fail(FD_ERR_UNSUPPORTED, "%s dtype %d not supported", name, t->dtype);
+    FD_TRY(check_ptr(t->data, 16, name));
+    const int64_t esz = int64_t(elem_bytes(t->dtype));
+    for (int i = 0; i < ndim; ++i)
+        if (t->shape[i] <= 0)
+            return fail(FD_ERR_INVALID_ARG, "%s shape[%d] = %lld is not positive", name, i, (long long)t->shape[i]);
+    if (t->stride[ndim - 1] != 1)
+        return fail(FD_ERR_UNSUPPORTED, "%s: the last dimension must be contiguous (stride %lld)", name,
+                    (long long)t->stride[ndim - 1]);
+    for (int i = 0; i < ndim - 1; ++i) {
+        if (t->stride[i] < 0)
+            return fail(FD_ERR_UNSUPPORTED, "%s stride[%d] = %lld is negative", name, i, (long long)t->stride[i]);
+        if ((t->stride[i] * esz) % 16 != 0)
+            return fail(FD_ERR_INVALID_ARG, "%s stride[%d] = %lld elements is not a multiple of 16 bytes", name, i,
+                        (long long)t->stride[i]);
+    }
+    return FD_OK;
+}
+
+bool same_layout(const fd_tensor* a, const fd_tensor* b) {
+    for (int i = 0; i < a->ndim; ++i)
+        if (a->shape[i] != b->shape[i] || a->stride[i] != b->stride[i]) return false;
+    return a->ndim == b->ndim && a->dtype == b->dtype;
+}
+
+// An output [B, H, D] whose rows do not overlap: the row dimensions,
+// ordered by stride, each step past everything the smaller ones span.
+bool rows_disjoint(const fd_tensor* o) {
+    int64_t s[2] = {o->stride[0], o->stride[1]}, n[2] = {o->shape[0], o->shape[1]};
+    if (s[0] > s[1]) {
+        std::swap(s[0], s[1]);
+        std::swap(n[0], n[1]);
+    }
+    int64_t span = o->shape[2];
+    for (int i = 0; i < 2; ++i) {
+        if (n[i] == 1) continue;
+        if (s[i] < span) return false;
+        span = s[i] * n[i];
+    }
+    return true;
+}
+
+// Row stride of a KV cache (token dimension `dim`) within what the
+// kernels' 32-bit row offsets reach.
+fd_status check_row_stride(const fd_tensor* t, int dim, const char* name) {
+    const int64_t st = t->stride[dim];
+    if (st > kMaxRowStride || st * int64_t(elem_bytes(t->dtype)) > kMaxRowStrideBytes)
+        return fail(FD_ERR_UNSUPPORTED, "%s row stride %lld is not below 2^24 elements and 2^27 bytes", name,
+                    (long long)st);
+    return FD_OK;
 }
 
 }  // namespace
@@ -269,6 +345,18 @@ static fd_status resolve_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, i
     return FD_OK;
 }
 
+// Work units (one workgroup each) and output rows of one decode call must
+// stay below 2^30: the kernels index them with 32-bit integers.
+static fd_status check_grid(int32_t B, int32_t Hq, int32_t Hkv, int row_blocks, int32_t ns) {
+    const int64_t units = int64_t(B) * Hkv * row_blocks * ns;
+    if (units >= kMaxUnits)
+        return fail(FD_ERR_UNSUPPORTED, "%lld work units (batch %d x %d KV heads x %d row blocks x %d pieces) "
+                    "reach the 2^30 limit", (long long)units, B, Hkv, row_blocks, ns);
+    if (int64_t(B) * Hq >= kMaxUnits)
+        return fail(FD_ERR_UNSUPPORTED, "batch %d x %d query heads reach the 2^30 row limit", B, Hq);
+    return FD_OK;
+}
+
 fd_status fd_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lmax,
                                         int32_t dtype, int32_t n_splits, size_t* bytes) {
     if (!bytes) return fail(FD_ERR_INVALID_ARG, "bytes is NULL");
@@ -285,7 +373,8 @@ fd_status fd_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
 static fd_status run_decode(fd::PartialParams p, const void* q, const int32_t* lens, int32_t B, int32_t Hq,
                             int32_t Hkv, int32_t D, int64_t Lmax, int32_t dtype, int32_t n_splits,
                             void* out, int32_t out_dtype, float* lse_out, float scale, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, const IoStrides& io,
+                            int32_t force = FD_TESTING_KERNEL_AUTO) {
     FD_TRY(check_out_dtype(out_dtype));
     FD_TRY(check_ptr(q, 16, "q"));
     FD_TRY(check_ptr(out, 16, "out"));
@@ -304,8 +393,13 @@ static fd_status run_decode(fd::PartialParams p, const void* q, const int32_t* l
             return fail(FD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total());
     }
 
-    const Path path = choose_path(dtype, D, Hq / Hkv);
+    const Path path = choose_path(dtype, D, Hq / Hkv, force);
+    FD_TRY(check_grid(B, Hq, Hkv, path.row_blocks, ns));
     p.q = q;
+    p.q_stride_b = io.q_b;
+    p.q_stride_h = io.q_h;
+    p.out_stride_b = io.out_b;
+    p.out_stride_h = io.out_h;
     p.lens = lens;
     p.out = out;
     p.lse_out = lse_out;
@@ -333,10 +427,14 @@ static fd_status run_decode(fd::PartialParams p, const void* q, const int32_t* l
         p.part_offset = 0;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    FD_TRY(fd::validate_lens(lens, B, 1, Lmax, "lens (each in [1, max_len])", s));
+    if (p.block_table)
+        FD_TRY(fd::validate_table(p.block_table, lens, B, int32_t(p.bt_stride), 1 << p.page_shift, Lmax, p.n_pages, s));
     hipError_t e = launch_partial(p, path, dtype, D, s);
     if (e != hipSuccess) return hip_fail(e, "split-KV partial kernel launch");
     if (ns > 1) {
-        e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), ns, D, out, p.out_bf16, lse_out, s);
+        e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), ns, D, out, fd::OutRows{Hq, io.out_b, io.out_h},
+                                   p.out_bf16, lse_out, s);
         if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
     }
     return FD_OK;
@@ -354,10 +452,11 @@ fd_status fd_decode_attn(const void* q, const void* k, const void* v, const int3
     fd::PartialParams p{};
     p.k = k;
     p.v = v;
+    p.kv_stride_t = D;
     p.kv_stride_h = Lmax * D;
     p.kv_stride_b = int64_t(Hkv) * Lmax * D;
     return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream, dense_io(Hq, D));
 }
 
 fd_status fd_decode_attn_fp8(const void* q, const void* k, const void* v, const float* k_scale,
@@ -373,12 +472,40 @@ fd_status fd_decode_attn_fp8(const void* q, const void* k, const void* v, const 
     fd::PartialParams p{};
     p.k = k;
     p.v = v;
+    p.kv_stride_t = D;
     p.kv_stride_h = Lmax * D;
     p.kv_stride_b = int64_t(Hkv) * Lmax * D;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
     return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, FD_FP8_E4M3, n_splits, out, out_dtype, lse_out, scale,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream, dense_io(Hq, D));
+}
+
+// Page-pool addressing shared by the paged entry points ([MW] PagedAttention
+// paragraph): pool [num_pages, Hkv, page_size, D], table [B, max_pages].
+static fd_status paged_addressing(const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                  int32_t Hkv, int32_t D, int32_t page_size, int64_t num_pages, int32_t max_pages,
+                                  fd::PartialParams* p) {
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [16, 2^20]", page_size);
+    if (num_pages <= 0 || num_pages > INT32_MAX)
+        return fail(FD_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31 - 1]", (long long)num_pages);
+    if (max_pages <= 0) return fail(FD_ERR_INVALID_ARG, "max_pages_per_seq must be positive (got %d)", max_pages);
+    FD_TRY(check_ptr(k_pages, 16, "k_pages"));
+    FD_TRY(check_ptr(v_pages, 16, "v_pages"));
+    FD_TRY(check_ptr(block_table, 4, "block_table"));
+    p->k = k_pages;
+    p->v = v_pages;
+    p->block_table = block_table;
+    p->bt_stride = max_pages;
+    p->kv_stride_t = D;
+    p->kv_stride_h = int64_t(page_size) * D;
+    p->page_stride = int64_t(Hkv) * page_size * D;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    p->page_shift = shift;
+    p->n_pages = int32_t(num_pages);
+    return FD_OK;
 }
 
 fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -387,30 +514,13 @@ fd_status fd_decode_attn_paged(const void* q, const void* k_pages, const void* v
                                int32_t max_pages, int32_t dtype, int32_t n_splits, void* out,
                                int32_t out_dtype, float* lse_out, float scale, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
-        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [16, 2^20]", page_size);
-    if (num_pages <= 0 || num_pages > INT32_MAX)
-        return fail(FD_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31 - 1]", (long long)num_pages);
-    if (max_pages <= 0) return fail(FD_ERR_INVALID_ARG, "max_pages_per_seq must be positive (got %d)", max_pages);
-    const int64_t Lmax = int64_t(max_pages) * page_size;
     if (dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "paged calls take fp32 or bf16 caches");
-    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
-    FD_TRY(check_ptr(k_pages, 16, "k_pages"));
-    FD_TRY(check_ptr(v_pages, 16, "v_pages"));
-    FD_TRY(check_ptr(block_table, 4, "block_table"));
     fd::PartialParams p{};
-    p.k = k_pages;
-    p.v = v_pages;
-    p.block_table = block_table;
-    p.bt_stride = max_pages;
-    p.kv_stride_h = int64_t(page_size) * D;
-    p.page_stride = int64_t(Hkv) * page_size * D;
-    int shift = 0;
-    while ((1 << shift) < page_size) ++shift;
-    p.page_shift = shift;
-    p.n_pages = int32_t(num_pages);
+    FD_TRY(paged_addressing(k_pages, v_pages, block_table, Hkv, D, page_size, num_pages, max_pages, &p));
+    const int64_t Lmax = int64_t(max_pages) * page_size;
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
     return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream, dense_io(Hq, D));
 }
 
 int32_t fd_piece_tile_rows(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
@@ -441,12 +551,16 @@ fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, c
     if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
 
     const Path path = choose_path(dtype, D, Hq / Hkv);
+    FD_TRY(check_grid(B, Hq, Hkv, path.row_blocks, n_splits));
     fd::PartialParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
+    p.q_stride_b = int64_t(Hq) * D;
+    p.q_stride_h = D;
     p.lens = lens;
     p.Lmax = Lmax;
+    p.kv_stride_t = D;
     p.kv_stride_h = Lmax * D;
     p.kv_stride_b = int64_t(Hkv) * Lmax * D;
     p.B = B;
@@ -461,6 +575,7 @@ fd_status fd_decode_attn_partials(const void* q, const void* k, const void* v, c
     p.lse_part = lse_part;
     p.part_stride = n_splits;
     p.part_offset = 0;
+    FD_TRY(fd::validate_lens(lens, B, 1, Lmax, "lens (each in [1, max_len])", static_cast<hipStream_t>(stream)));
     hipError_t e = launch_partial(p, path, dtype, D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "split-KV partial kernel launch");
     return FD_OK;
@@ -497,18 +612,21 @@ fd_status fd_bifurcated_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
     return FD_OK;
 }
 
-fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx, const void* k_dec,
-                             const void* v_dec, const int32_t* dec_lens, int32_t S, int32_t Hq,
-                             int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld, int32_t dtype, void* out,
-                             int32_t out_dtype, float* lse_out, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Shared body of the bifurcated entry points.  `dk` carries the decode
+// cache's addressing (k, v and dense strides, or the page pool and table);
+// the context is [Hkv, Lc, D] with row stride ctx_t and head stride ctx_h.
+static fd_status run_bifurcated(const void* q, const IoStrides& io, const void* k_ctx, const void* v_ctx,
+                                int64_t ctx_h, int64_t ctx_t, fd::PartialParams dk, const int32_t* dec_lens,
+                                int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld,
+                                int32_t dtype, void* out, int32_t out_dtype, float* lse_out, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
     FD_TRY(check_bifurcated_shapes(S, Hq, Hkv, D, Lc, Ld, dtype));
     FD_TRY(check_out_dtype(out_dtype));
     FD_TRY(check_ptr(q, 16, "q"));
     FD_TRY(check_ptr(k_ctx, 16, "k_ctx"));
     FD_TRY(check_ptr(v_ctx, 16, "v_ctx"));
-    FD_TRY(check_ptr(k_dec, 16, "k_dec"));
-    FD_TRY(check_ptr(v_dec, 16, "v_dec"));
+    FD_TRY(check_ptr(dk.k, 16, "k_dec"));
+    FD_TRY(check_ptr(dk.v, 16, "v_dec"));
     FD_TRY(check_ptr(out, 16, "out"));
     if (dec_lens && !aligned(dec_lens, 4)) return fail(FD_ERR_INVALID_ARG, "dec_lens is not 4-byte aligned");
     if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
@@ -523,6 +641,7 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     const int32_t P = pc + pd;
     if (P > FD_MAX_PARTS) return fail(FD_ERR_UNSUPPORTED, "%d pieces exceed the combine limit %d", P, FD_MAX_PARTS);
     const int64_t rows = int64_t(S) * Hq;
+    if (rows >= kMaxUnits) return fail(FD_ERR_UNSUPPORTED, "samples %d x %d query heads reach the 2^30 row limit", S, Hq);
     const PartialLayout L = partial_layout(rows, P, D);
     if (workspace_bytes < L.total())
         return fail(FD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total());
@@ -530,10 +649,17 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_bytes);
 
     const Path path = choose_path(dtype, D, Hq / Hkv);
+    FD_TRY(check_grid(S, Hq, Hkv, path.row_blocks, std::max(pc, pd)));
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    fd::PartialParams p{};
+    FD_TRY(fd::validate_lens(dec_lens, S, 0, Ld, "dec_lens (each in [0, dec_max_len])", s));
+    if (dk.block_table)
+        FD_TRY(fd::validate_table(dk.block_table, dec_lens, S, int32_t(dk.bt_stride), 1 << dk.page_shift, Ld,
+                                  dk.n_pages, s));
+    fd::PartialParams p = dk;   // decode cache addressing
     p.q = q;
+    p.q_stride_b = io.q_b;
+    p.q_stride_h = io.q_h;
     p.o_part = o_part;
     p.lse_part = lse_part;
     p.B = S;
@@ -551,8 +677,12 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
         // split-KV unit with 16-row blocks.
         fd::BifContextParams c{};
         c.q = q;
+        c.q_stride_b = io.q_b;
+        c.q_stride_h = io.q_h;
         c.k_ctx = k_ctx;
         c.v_ctx = v_ctx;
+        c.ctx_stride_h = ctx_h;
+        c.ctx_stride_t = ctx_t;
         c.o_part = o_part;
         c.lse_part = lse_part;
         c.S = S;
@@ -564,12 +694,8 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
         c.part_stride = P;
         c.part_offset = 0;
         c.scale_log2 = p.scale_log2;
-        p.k = k_dec;
-        p.v = v_dec;
         p.lens = dec_lens;
         p.Lmax = Ld;
-        p.kv_stride_h = Ld * D;
-        p.kv_stride_b = int64_t(Hkv) * Ld * D;
         p.n_splits = pd;
         p.part_offset = pc;
         p.row_blocks = (Hq / Hkv + 15) / 16;
@@ -578,32 +704,60 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
     } else {
         // Context part through the split-KV kernel: every sample reads the
         // same [Hkv, Lc, D] rows (batch stride 0); all Lc rows are valid.
-        p.k = k_ctx;
-        p.v = v_ctx;
-        p.lens = nullptr;
-        p.Lmax = Lc;
-        p.kv_stride_b = 0;
-        p.kv_stride_h = Lc * D;
-        p.n_splits = pc;
-        p.part_offset = 0;
-        e = launch_partial(p, path, dtype, D, s);
+        fd::PartialParams pcx = p;
+        pcx.k = k_ctx;
+        pcx.v = v_ctx;
+        pcx.block_table = nullptr;
+        pcx.lens = nullptr;
+        pcx.Lmax = Lc;
+        pcx.kv_stride_b = 0;
+        pcx.kv_stride_h = ctx_h;
+        pcx.kv_stride_t = ctx_t;
+        pcx.n_splits = pc;
+        pcx.part_offset = 0;
+        e = launch_partial(pcx, path, dtype, D, s);
         if (e != hipSuccess) return hip_fail(e, "bifurcated context kernel launch");
         // Decode part: each sample's own rows, dec_lens[s] of them (0 allowed).
-        p.k = k_dec;
-        p.v = v_dec;
         p.lens = dec_lens;
         p.Lmax = Ld;
-        p.kv_stride_h = Ld * D;
-        p.kv_stride_b = int64_t(Hkv) * Ld * D;
         p.n_splits = pd;
         p.part_offset = pc;
         e = launch_partial(p, path, dtype, D, s);
         if (e != hipSuccess) return hip_fail(e, "bifurcated decode kernel launch");
     }
 
-    e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), P, D, out, out_dtype == FD_BF16, lse_out, s);
+    e = fd::launch_lse_combine(o_part, lse_part, int32_t(rows), P, D, out, fd::OutRows{Hq, io.out_b, io.out_h},
+                               out_dtype == FD_BF16, lse_out, s);
     if (e != hipSuccess) return hip_fail(e, "bifurcated combine kernel launch");
     return FD_OK;
+}
+
+fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx, const void* k_dec,
+                             const void* v_dec, const int32_t* dec_lens, int32_t S, int32_t Hq,
+                             int32_t Hkv, int32_t D, int64_t Lc, int64_t Ld, int32_t dtype, void* out,
+                             int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    fd::PartialParams dk{};
+    dk.k = k_dec;
+    dk.v = v_dec;
+    dk.kv_stride_t = D;
+    dk.kv_stride_h = Ld * D;
+    dk.kv_stride_b = int64_t(Hkv) * Ld * D;
+    return run_bifurcated(q, dense_io(Hq, D), k_ctx, v_ctx, Lc * D, D, dk, dec_lens, S, Hq, Hkv, D, Lc, Ld, dtype,
+                          out, out_dtype, lse_out, scale, workspace, workspace_bytes, stream);
+}
+
+fd_status fd_bifurcated_attn_paged(const void* q, const void* k_ctx, const void* v_ctx, const void* k_pages,
+                                   const void* v_pages, const int32_t* block_table, const int32_t* dec_lens,
+                                   int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t Lc, int32_t page_size,
+                                   int64_t num_pages, int32_t max_pages_per_seq, int32_t dtype, void* out,
+                                   int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    fd::PartialParams dk{};
+    FD_TRY(paged_addressing(k_pages, v_pages, block_table, Hkv, D, page_size, num_pages, max_pages_per_seq, &dk));
+    const int64_t Ld = int64_t(max_pages_per_seq) * page_size;
+    return run_bifurcated(q, dense_io(Hq, D), k_ctx, v_ctx, Lc * D, D, dk, dec_lens, S, Hq, Hkv, D, Lc, Ld, dtype,
+                          out, out_dtype, lse_out, scale, workspace, workspace_bytes, stream);
 }
 
 fd_status fd_prefill_attn(const void* q, const void* k, const void* v, const int32_t* lens, int32_t B,
@@ -638,6 +792,7 @@ fd_status fd_prefill_attn(const void* q, const void* k, const void* v, const int
     p.out_bf16 = out_dtype == FD_BF16;
     if (int64_t(B) * Hkv * p.n_ptiles >= (int64_t(1) << 30))
         return fail(FD_ERR_UNSUPPORTED, "too many prefill work units");
+    FD_TRY(fd::validate_lens(lens, B, 1, Lmax, "lens (each in [1, max_len])", static_cast<hipStream_t>(stream)));
     hipError_t e = fd::launch_prefill(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     return FD_OK;
@@ -653,10 +808,122 @@ fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t row
     FD_TRY(check_ptr(lse_part, 4, "lse_part"));
     FD_TRY(check_ptr(out, out_dtype == FD_BF16 ? 2 : 4, "out"));
     if (lse_out && !aligned(lse_out, 4)) return fail(FD_ERR_INVALID_ARG, "lse_out is not 4-byte aligned");
-    hipError_t e = fd::launch_lse_combine(o_part, lse_part, rows, n_parts, D, out, out_dtype == FD_BF16,
+    hipError_t e = fd::launch_lse_combine(o_part, lse_part, rows, n_parts, D, out, fd::OutRows{1, D, 0},
+                                          out_dtype == FD_BF16,
                                           lse_out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "lse combine kernel launch");
     return FD_OK;
+}
+
+fd_status fd_testing_decode_attn(const void* q, const void* k, const void* v, const float* k_scale,
+                                 const float* v_scale, const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int64_t Lmax, int32_t dtype, int32_t n_splits, void* out,
+                                 int32_t out_dtype, float* lse_out, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream, int32_t partial_kernel) {
+    if (partial_kernel != FD_TESTING_KERNEL_AUTO && partial_kernel != FD_TESTING_KERNEL_VALU &&
+        partial_kernel != FD_TESTING_KERNEL_MFMA)
+        return fail(FD_ERR_INVALID_ARG, "partial_kernel %d is not 0, 1 or 2", partial_kernel);
+    FD_TRY(check_decode_shapes(B, Hq, Hkv, D, Lmax, dtype, n_splits));
+    if (partial_kernel == FD_TESTING_KERNEL_MFMA && !mfma_supported(dtype, D))
+        return fail(FD_ERR_UNSUPPORTED, "the matrix-core kernel takes bf16 or E4M3 caches with head_dim 128");
+    FD_TRY(check_ptr(k, 16, "k"));
+    FD_TRY(check_ptr(v, 16, "v"));
+    if (k_scale && !aligned(k_scale, 4)) return fail(FD_ERR_INVALID_ARG, "k_scale is not 4-byte aligned");
+    if (v_scale && !aligned(v_scale, 4)) return fail(FD_ERR_INVALID_ARG, "v_scale is not 4-byte aligned");
+    fd::PartialParams p{};
+    p.k = k;
+    p.v = v;
+    p.kv_stride_t = D;
+    p.kv_stride_h = Lmax * D;
+    p.kv_stride_b = int64_t(Hkv) * Lmax * D;
+    if (dtype == FD_FP8_E4M3) {
+        p.k_scale = k_scale;
+        p.v_scale = v_scale;
+    }
+    return run_decode(p, q, lens, B, Hq, Hkv, D, Lmax, dtype, n_splits, out, out_dtype, lse_out, scale,
+                      workspace, workspace_bytes, stream, dense_io(Hq, D), partial_kernel);
+}
+
+fd_status fd_decode_attn_strided(const fd_tensor* q, const fd_tensor* k, const fd_tensor* v, const float* k_scale,
+                                 const float* v_scale, const int32_t* lens, int32_t n_splits, const fd_tensor* out,
+                                 float* lse_out, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    FD_TRY(check_tensor(q, 3, "q"));
+    FD_TRY(check_tensor(k, 4, "k"));
+    FD_TRY(check_tensor(v, 4, "v"));
+    FD_TRY(check_tensor(out, 3, "out"));
+    const int64_t B = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+    const int64_t Hkv = k->shape[1], Lmax = k->shape[2];
+    if (k->shape[0] != B || k->shape[3] != D)
+        return fail(FD_ERR_INVALID_ARG, "k [%lld, %lld, %lld, %lld] does not match q [%lld, %lld, %lld]",
+                    (long long)k->shape[0], (long long)Hkv, (long long)Lmax, (long long)k->shape[3], (long long)B,
+                    (long long)Hq, (long long)D);
+    if (!same_layout(k, v)) return fail(FD_ERR_UNSUPPORTED, "k and v must share shape, strides and dtype");
+    if (out->shape[0] != B || out->shape[1] != Hq || out->shape[2] != D)
+        return fail(FD_ERR_INVALID_ARG, "out must be [B, Hq, D] like q");
+    if (!rows_disjoint(out)) return fail(FD_ERR_INVALID_ARG, "out strides make output rows overlap");
+    if (B > INT32_MAX || Hq > INT32_MAX || Hkv > INT32_MAX || D > INT32_MAX)
+        return fail(FD_ERR_INVALID_ARG, "dimension beyond int32");
+    const int32_t dtype = k->dtype;
+    if (dtype == FD_FP8_E4M3 ? q->dtype != FD_BF16 : q->dtype != dtype)
+        return fail(FD_ERR_UNSUPPORTED, "q dtype %d with a cache of dtype %d (same dtype, or bf16 q for E4M3)",
+                    q->dtype, dtype);
+    FD_TRY(check_decode_shapes(int32_t(B), int32_t(Hq), int32_t(Hkv), int32_t(D), Lmax, dtype, n_splits));
+    FD_TRY(check_row_stride(k, 2, "k"));
+    if (k_scale && !aligned(k_scale, 4)) return fail(FD_ERR_INVALID_ARG, "k_scale is not 4-byte aligned");
+    if (v_scale && !aligned(v_scale, 4)) return fail(FD_ERR_INVALID_ARG, "v_scale is not 4-byte aligned");
+    fd::PartialParams p{};
+    p.k = k->data;
+    p.v = v->data;
+    p.kv_stride_b = k->stride[0];
+    p.kv_stride_h = k->stride[1];
+    p.kv_stride_t = k->stride[2];
+    if (dtype == FD_FP8_E4M3) {
+        p.k_scale = k_scale;
+        p.v_scale = v_scale;
+    }
+    const IoStrides io{q->stride[0], q->stride[1], out->stride[0], out->stride[1]};
+    return run_decode(p, q->data, lens, int32_t(B), int32_t(Hq), int32_t(Hkv), int32_t(D), Lmax, dtype, n_splits,
+                      out->data, out->dtype, lse_out, scale, workspace, workspace_bytes, stream, io);
+}
+
+fd_status fd_bifurcated_attn_strided(const fd_tensor* q, const fd_tensor* k_ctx, const fd_tensor* v_ctx,
+                                     const fd_tensor* k_dec, const fd_tensor* v_dec, const int32_t* dec_lens,
+                                     const fd_tensor* out, float* lse_out, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    FD_TRY(check_tensor(q, 3, "q"));
+    FD_TRY(check_tensor(k_ctx, 3, "k_ctx"));
+    FD_TRY(check_tensor(v_ctx, 3, "v_ctx"));
+    FD_TRY(check_tensor(k_dec, 4, "k_dec"));
+    FD_TRY(check_tensor(v_dec, 4, "v_dec"));
+    FD_TRY(check_tensor(out, 3, "out"));
+    const int64_t S = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+    const int64_t Hkv = k_ctx->shape[0], Lc = k_ctx->shape[1], Ld = k_dec->shape[2];
+    if (k_ctx->shape[2] != D || k_dec->shape[0] != S || k_dec->shape[1] != Hkv || k_dec->shape[3] != D)
+        return fail(FD_ERR_INVALID_ARG, "k_ctx [Hkv, Lc, D] and k_dec [S, Hkv, Ldmax, D] do not match q [S, Hq, D]");
+    if (!same_layout(k_ctx, v_ctx) || !same_layout(k_dec, v_dec))
+        return fail(FD_ERR_UNSUPPORTED, "k and v of the context (and of the decode part) must share shape, strides "
+                    "and dtype");
+    if (out->shape[0] != S || out->shape[1] != Hq || out->shape[2] != D)
+        return fail(FD_ERR_INVALID_ARG, "out must be [S, Hq, D] like q");
+    if (!rows_disjoint(out)) return fail(FD_ERR_INVALID_ARG, "out strides make output rows overlap");
+    if (S > INT32_MAX || Hq > INT32_MAX || Hkv > INT32_MAX || D > INT32_MAX)
+        return fail(FD_ERR_INVALID_ARG, "dimension beyond int32");
+    const int32_t dtype = q->dtype;
+    if (k_ctx->dtype != dtype || k_dec->dtype != dtype)
+        return fail(FD_ERR_UNSUPPORTED, "q, context and decode caches must share one dtype");
+    FD_TRY(check_row_stride(k_ctx, 1, "k_ctx"));
+    FD_TRY(check_row_stride(k_dec, 2, "k_dec"));
+    fd::PartialParams dk{};
+    dk.k = k_dec->data;
+    dk.v = v_dec->data;
+    dk.kv_stride_b = k_dec->stride[0];
+    dk.kv_stride_h = k_dec->stride[1];
+    dk.kv_stride_t = k_dec->stride[2];
+    const IoStrides io{q->stride[0], q->stride[1], out->stride[0], out->stride[1]};
+    return run_bifurcated(q->data, io, k_ctx->data, v_ctx->data, k_ctx->stride[0], k_ctx->stride[1], dk, dec_lens,
+                          int32_t(S), int32_t(Hq), int32_t(Hkv), int32_t(D), Lc, Ld, dtype, out->data, out->dtype,
+                          lse_out, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

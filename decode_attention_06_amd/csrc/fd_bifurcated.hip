@@ -76,16 +76,16 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             u32x4_t v = {0u, 0u, 0u, 0u};
-            if (rho < nrows) {
-                const int64_t row = (int64_t)(rho / G) * p.Hq + kvh * G + rho % G;
-                v = ld16(static_cast<const uint16_t*>(p.q) + row * MF_D + 32 * s + 8 * g);
-            }
+            if (rho < nrows)
+                v = ld16(static_cast<const uint16_t*>(p.q) + (int64_t)(rho / G) * p.q_stride_b +
+                         (int64_t)(kvh * G + rho % G) * p.q_stride_h + 32 * s + 8 * g);
             qb[r][s] = as_bf16x8(v);
         }
     }
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(p.k_ctx) + (int64_t)kvh * p.Lc * MF_D;
-    const uint16_t* vbase = static_cast<const uint16_t*>(p.v_ctx) + (int64_t)kvh * p.Lc * MF_D;
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k_ctx) + (int64_t)kvh * p.ctx_stride_h;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v_ctx) + (int64_t)kvh * p.ctx_stride_h;
+    const int rs = (int)p.ctx_stride_t;   // elements from one context row to the next
     const int ktok0 = 8 * (i >> 2) + (i & 3);
     const float sl2 = p.scale_log2;
 
@@ -117,10 +117,10 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
         u32x4_t kr[2][4], vt[8];
 #pragma unroll
         for (int t = 0; t < CTX_STAGES - 1; ++t)
-            issue_tile<NW>(kbase, vbase, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
+            issue_tile<NW>(kbase, vbase, rs, c0 + t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
         wait_vm<TWO_TILES>();
         ring_barrier();
-        const TileAddrs a0 = ring_step<NW>(kbase, vbase, c0 + (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
+        const TileAddrs a0 = ring_step<NW>(kbase, vbase, rs, c0 + (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
                                        ks[CTX_STAGES - 1], vs[CTX_STAGES - 1], ks[0], vs[0], ktok0, g, i, kr, vt);
         keep_addrs<NW>(a0);
         for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
@@ -131,7 +131,7 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
                 if (t + 1 >= n_tiles) break;
                 wait_vm<TWO_TILES>();
                 ring_barrier();
-                const TileAddrs an = ring_step<NW>(kbase, vbase, c0 + (t + CTX_STAGES) * CTX_TILE, c1, wave, lane,
+                const TileAddrs an = ring_step<NW>(kbase, vbase, rs, c0 + (t + CTX_STAGES) * CTX_TILE, c1, wave, lane,
                                                ks[st], vs[st], ks[(st + 1) % CTX_STAGES], vs[(st + 1) % CTX_STAGES],
                                                ktok0, g, i, kr, vt);
                 keep_addrs<NW>(an);
@@ -166,13 +166,17 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
 
 // The bifurcated call as one launch with two workgroup roles: context
 // units (above) and the decode part's split-KV units (16-row matrix-core
-// blocks, one piece per unit).  Workgroup ids come in blocks of eight
-// (consecutive ids go to the eight XCDs in turn).  When the decode units are
-// few, blocks alternate between the roles in proportion to their counts, so
-// both kinds run side by side from the start -- the decode part streams its
-// own KV from HBM while the context part keeps the matrix cores busy; when
-// they are many, the context blocks come first.  Either way a context
-// unit's row tiles share one XCD.
+// blocks, one piece per unit; dense or paged decode cache).  Workgroup ids
+// come in blocks of eight (consecutive ids go to the eight XCDs in turn).
+// When the decode units are few, blocks alternate between the roles in
+// proportion to their counts, so both kinds run side by side from the start
+// -- the decode part streams its own KV from HBM while the context part
+// keeps the matrix cores busy; when they are many, the context blocks come
+// first.  Either way a context unit's row tiles share one XCD, and so do
+// the row blocks of one decode unit (sample, KV head), which also start
+// together: the second reads the decode rows the first brings into that
+// XCD's L2 instead of fetching them again.
+template <bool PAGED, bool PACK>
 __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextParams c, const PartialParams d,
                                                             int n_ctx, int n_dec) {
     __shared__ __attribute__((aligned(16))) char lds[CTX_LDS_BYTES];
@@ -195,8 +199,15 @@ __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextPara
         const int cid = ctx_before * XCDS + lane8;
         if (cid < n_ctx) context_body<4>(c, cid, lds);
     } else {
+        // Decode id -> (unit, row block): ids congruent mod 8 share an XCD;
+        // the row blocks of a unit take consecutive ids of one residue.
         const int did = (blk - ctx_before) * XCDS + lane8;
-        if (did < n_dec) partial_mfma_body<1, 4>(d, did, *reinterpret_cast<PartialLds<1, 4>*>(lds));
+        const int rb = d.row_blocks;
+        const int q = did / XCDS;
+        const int unit = (q / rb) * XCDS + did % XCDS;
+        if (did < n_dec && unit < d.B * d.Hkv)
+            partial_mfma_body<1, 4, PAGED, false, PACK>(d, unit * rb + q % rb,
+                                                       *reinterpret_cast<PartialLds<1, 4>*>(lds));
     }
 }
 
@@ -208,12 +219,28 @@ int bif_context_row_tiles(int S, int G) {
 }
 
 hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, hipStream_t stream) {
+    // The decode role takes one piece per (sample, KV head); its ids are
+    // padded to whole groups of eight units.
+    if (d.n_splits != 1) return hipErrorInvalidValue;
     const int units = c.Hkv * c.n_pieces;
     const int64_t n_ctx = (int64_t)((units + XCDS - 1) / XCDS) * XCDS * c.row_tiles;
-    const int64_t n_dec = (int64_t)d.B * d.Hkv * d.row_blocks * d.n_splits;
+    const int64_t dec_units = (int64_t)d.B * d.Hkv;
+    const int64_t n_dec = (dec_units + XCDS - 1) / XCDS * XCDS * d.row_blocks;
     const int64_t wgs = ((n_ctx + XCDS - 1) / XCDS + (n_dec + XCDS - 1) / XCDS) * XCDS;
     if (n_ctx >= (1 << 30) || n_dec >= (1 << 30)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bifurcated_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, c, d, (int)n_ctx, (int)n_dec);
+    // Groups of at most 8 query heads: the decode role packs its weight
+    // remainders into the 16-row block's padding columns.
+    const bool pack = d.Hq / d.Hkv <= 8;
+#define FD_BIF(PG, PK) hipLaunchKernelGGL((bifurcated_kernel<PG, PK>), dim3((unsigned)wgs), dim3(256), 0, stream, c, d, \
+                                          (int)n_ctx, (int)n_dec)
+    if (d.block_table) {
+        if (pack) FD_BIF(true, true);
+        else FD_BIF(true, false);
+    } else {
+        if (pack) FD_BIF(false, true);
+        else FD_BIF(false, false);
+    }
+#undef FD_BIF
     return hipGetLastError();
 }
 

@@ -13,6 +13,17 @@ namespace fd {
 // the status through (printf-style format).
 fd_status set_error(fd_status s, const char* fmt, ...);
 
+// Device-side validation (FD_VALIDATE=1 or fd_set_validation(1)): count the
+// entries of a device array outside their range, synchronise, and return
+// FD_ERR_INVALID_ARG naming the first; FD_OK at once when validation is off.
+bool validation_on();
+// lens[0 .. n) must lie in [lo, hi].
+fd_status validate_lens(const int32_t* lens, int64_t n, int64_t lo, int64_t hi, const char* what, hipStream_t s);
+// Entries of table [B, cols] that cover rows below lens[b] (or `rows`) must
+// lie in [0, n_pages).
+fd_status validate_table(const int32_t* table, const int32_t* lens, int32_t B, int32_t cols, int32_t page_size,
+                         int64_t rows, int32_t n_pages, hipStream_t s);
+
 // Most pieces one combine can merge per output row (LDS holds their weights).
 #define FD_MAX_PARTS 4096
 
@@ -21,17 +32,20 @@ fd_status set_error(fd_status s, const char* fmt, ...);
 // piece of the KV rows once and keeps a running max / running sum per query
 // row (the online softmax).
 struct PartialParams {
-    const void* q;          // [B, Hq, D]
-    const void* k;          // dense: element (b, kvh, t, d) at b*kv_stride_b + kvh*kv_stride_h + t*D + d
+    const void* q;          // [B, Hq, D]: element (b, h, d) at b*q_stride_b + h*q_stride_h + d
+    const void* k;          // dense: element (b, kvh, t, d) at b*kv_stride_b + kvh*kv_stride_h + t*kv_stride_t + d
     const void* v;          // paged: see block_table
     const int32_t* lens;    // [B] valid rows per sequence, or nullptr = Lmax
-    void* out;              // direct mode: final output [B, Hq, D]
+    void* out;              // direct mode: final output [B, Hq, D] at b*out_stride_b + h*out_stride_h + d
     float* lse_out;         // direct mode: [B, Hq] natural-log lse, or nullptr
     float* o_part;          // partial mode: [B*Hq, part_stride, D]
     float* lse_part;        // partial mode: [B*Hq, part_stride]
     int64_t Lmax;           // rows available per (b, kv head)
     int64_t kv_stride_b;    // elements; 0 makes every sequence read the same KV
     int64_t kv_stride_h;    // elements
+    int64_t kv_stride_t;    // elements between consecutive rows (dense caches; pages hold rows D apart)
+    int64_t q_stride_b, q_stride_h;       // elements
+    int64_t out_stride_b, out_stride_h;   // elements
     int32_t B, Hq, Hkv;
     int32_t n_splits;       // pieces per sequence in this launch
     int32_t row_blocks;     // query-row blocks per KV head (G / rows per block)
@@ -64,9 +78,11 @@ struct PartialParams {
 // cut into n_pieces pieces; writes pieces [part_offset, part_offset +
 // n_pieces) of every row.
 struct BifContextParams {
-    const void* q;          // [S, Hq, D]
-    const void* k_ctx;      // [Hkv, Lc, D]
+    const void* q;          // [S, Hq, D] at s*q_stride_b + h*q_stride_h + d
+    const void* k_ctx;      // [Hkv, Lc, D] at kvh*ctx_stride_h + t*ctx_stride_t + d
     const void* v_ctx;
+    int64_t q_stride_b, q_stride_h;
+    int64_t ctx_stride_h, ctx_stride_t;
     float* o_part;          // [S*Hq, part_stride, D]
     float* lse_part;        // [S*Hq, part_stride]
     int32_t S, Hq, Hkv, Lc;
@@ -143,8 +159,16 @@ hipError_t launch_partial_valu(const PartialParams& p, int dtype, int head_dim, 
 // one word written to sink[0] only if it equals a sentinel.
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+// Where the combine writes output row r (= b * hq + h of a [B, hq, D]
+// output): element (r / hq) * stride_b + (r % hq) * stride_h + d.  A dense
+// [rows, D] output is {1, D, 0}.
+struct OutRows {
+    int32_t hq;
+    int64_t stride_b, stride_h;
+};
+
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
-                              int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
+                              int32_t n_parts, int32_t head_dim, void* out, OutRows out_rows, int32_t out_bf16,
                               float* lse_out, hipStream_t stream);
 
 }  // namespace fd

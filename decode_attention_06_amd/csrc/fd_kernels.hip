@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
     float qf[GB][EPL];
 #pragma unroll
     for (int g = 0; g < GB; ++g) {
-        const TQ* qp = static_cast<const TQ*>(p.q) + ((int64_t)b * p.Hq + h0 + g) * D + c * EPL;
+        const TQ* qp = static_cast<const TQ*>(p.q) + (int64_t)b * p.q_stride_b + (int64_t)(h0 + g) * p.q_stride_h +
+                       c * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; e += Vec16<TQ>::N)
             Vec16<TQ>::unpack(*reinterpret_cast<const uint4*>(qp + e), &qf[g][e]);
@@ -183,13 +184,16 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
 
     // Rows are addressed per 16-row group: a wave-uniform 64-bit base (the
     // dense slice's row, or the row's page) plus a 32-bit lane offset below
-    // 16 rows of D elements, so each load takes one offset register.  A wave
-    // tile covers NG groups; the rows of load u lie in group u * RPW / 16.
+    // 16 rows (the host keeps 16 row strides below 2^31 bytes), so each load
+    // takes one offset register.  A wave tile covers NG groups; the rows of
+    // load u lie in group u * RPW / 16.  Pages hold their rows D apart.
     const char* kpool = static_cast<const char*>(p.k);
     const char* vpool = static_cast<const char*>(p.v);
     const int64_t slice = PAGED ? 0 : kv_row_offset<false, D>(p, b, kvh, 0);
     constexpr int SZ = Vec16<T>::BYTES;
     const uint32_t lane_off = c * EPL * (uint32_t)SZ;
+    const int64_t row_st = PAGED ? (int64_t)D : p.kv_stride_t;      // elements between rows, below 2^24
+    const uint32_t row_st32 = (uint32_t)row_st;
     constexpr int NG = WAVE_TOK >= 16 ? WAVE_TOK / 16 : 1;
     static_assert(16 % RPW == 0, "a load's rows must stay inside one 16-row group");
 
@@ -231,14 +235,14 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
                 gb[h] = kv_page_offset<D>(p, gid[h], kvh, gs[h]) * (int64_t)SZ;
             } else {
                 gs[h] = kv_group_start(tb + 16 * h, t1 - 1);
-                gb[h] = (slice + (int64_t)gs[h] * D) * (int64_t)SZ;
+                gb[h] = (slice + (int64_t)gs[h] * row_st) * (int64_t)SZ;
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int h = (NG > 1) ? (u * RPW) / 16 : 0;
             const int t = min(tb + u * RPW + r, t1 - 1);
-            const uint32_t off = (uint32_t)(t - gs[h]) * (uint32_t)(D * SZ) + lane_off;
+            const uint32_t off = __umul24((uint32_t)(t - gs[h]), row_st32) * (uint32_t)SZ + lane_off;
             kr[u] = ld_stream16(kpool + gb[h] + off);
             vr[u] = ld_stream16(vpool + gb[h] + off);
         }
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(const PartialParams p
         const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2f : -INFINITY;
         const int64_t row = (int64_t)b * p.Hq + h0 + g;
         if (p.direct) {
-            store_out(p.out, row * D + d, o, p.out_bf16);
+            store_out(p.out, (int64_t)b * p.out_stride_b + (int64_t)(h0 + g) * p.out_stride_h + d, o, p.out_bf16);
             if (d == 0 && p.lse_out) p.lse_out[row] = lse;
         } else {
             const int64_t slot = row * p.part_stride + p.part_offset + split;
@@ -456,11 +460,18 @@ __device__ __forceinline__ void load_vec(const float* src, float (&v)[VEC]) {
     }
 }
 
+// Element offset of output row `row` (see OutRows; rows stay below 2^30,
+// so the division is a 32-bit one).
+__device__ __forceinline__ int64_t out_row_offset(const OutRows& o, int64_t row) {
+    const int32_t r = (int32_t)row;
+    return (int64_t)(r / o.hq) * o.stride_b + (int64_t)(r % o.hq) * o.stride_h;
+}
+
 template <int VEC>
 __global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* __restrict__ o_part,
                                                                   const float* __restrict__ lse_part,
                                                                   int32_t n_parts, int32_t D, void* out,
-                                                                  int32_t out_bf16, float* lse_out) {
+                                                                  OutRows orows, int32_t out_bf16, float* lse_out) {
     constexpr int DL = CMB_SLICE / VEC;         // threads across the slice
     constexpr int GROUPS = CMB_THREADS / DL;    // part groups
     __shared__ float s_red[CMB_THREADS / 64];
@@ -553,7 +564,7 @@ __global__ __launch_bounds__(CMB_THREADS) void lse_combine_kernel(const float* _
             float a = 0.f;
 #pragma unroll
             for (int k = 0; k < GROUPS; ++k) a += s_acc[k][tid];
-            store_out(out, row * D + d, (Z > 0.f) ? a / Z : 0.f, out_bf16);
+            store_out(out, out_row_offset(orows, row) + d, (Z > 0.f) ? a / Z : 0.f, out_bf16);
             if (d == 0 && lse_out) lse_out[row] = (Z > 0.f) ? M + logf(Z) : -INFINITY;
         }
     }
@@ -573,7 +584,8 @@ constexpr int CMB4_BATCH = 4;                   // pieces per thread per batch
 
 __global__ __launch_bounds__(256) void lse_combine_v4_kernel(const float* __restrict__ o_part,
                                                              const float* __restrict__ lse_part, int32_t n_parts,
-                                                             int32_t D, void* out, int32_t out_bf16, float* lse_out) {
+                                                             int32_t D, void* out, OutRows orows, int32_t out_bf16,
+                                                             float* lse_out) {
     __shared__ float s_m[4], s_z[4];
     __shared__ float4 s_acc[4][CMB4_CV];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -653,7 +665,7 @@ __global__ __launch_bounds__(256) void lse_combine_v4_kernel(const float* __rest
             A.w += s_acc[w][tid].w;
         }
         const float inv = (Z > 0.f) ? 1.f / Z : 0.f;
-        const int64_t o0 = row * D + 4 * c4;
+        const int64_t o0 = out_row_offset(orows, row) + 4 * c4;
         store_out(out, o0, A.x * inv, out_bf16);
         store_out(out, o0 + 1, A.y * inv, out_bf16);
         store_out(out, o0 + 2, A.z * inv, out_bf16);
@@ -676,7 +688,7 @@ template <int NV>
 __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const float* __restrict__ o_part,
                                                                           const float* __restrict__ lse_part,
                                                                           int32_t rows, int32_t n_parts, int32_t D,
-                                                                          void* out, int32_t out_bf16,
+                                                                          void* out, OutRows orows, int32_t out_bf16,
                                                                           float* lse_out) {
     constexpr int PB = NV <= 2 ? 32 : (NV <= 4 ? 16 : 8);   // pieces per batch (64 loads in flight)
     const int lane = threadIdx.x & 63;
@@ -722,10 +734,11 @@ __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const 
         load(i0);
     }
     const float inv = (Z > 0.f) ? 1.f / Z : 0.f;
+    const int64_t o0 = out_row_offset(orows, row);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) store_out(out, row * D + d, acc[k] * inv, out_bf16);
+        if (d < D) store_out(out, o0 + d, acc[k] * inv, out_bf16);
     }
     if (lane == 0 && lse_out) lse_out[row] = (Z > 0.f) ? M + logf(Z) : -INFINITY;
 }
@@ -758,7 +771,9 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 
 template <typename T, int D, bool PAGED>
 hipError_t launch_valu_rows(const PartialParams& p, int rows_per_block, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks * p.n_splits));
+    const int64_t wgs = (int64_t)p.B * p.Hkv * p.row_blocks * p.n_splits;
+    if (wgs >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     const dim3 block(256);
     switch (rows_per_block) {
         case 1: hipLaunchKernelGGL((partial_valu_kernel<T, D, 1, PAGED>), grid, block, 0, stream, p); break;
@@ -806,7 +821,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
 }
 
 hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
-                              int32_t n_parts, int32_t head_dim, void* out, int32_t out_bf16,
+                              int32_t n_parts, int32_t head_dim, void* out, OutRows orows, int32_t out_bf16,
                               float* lse_out, hipStream_t stream) {
     // One wave per row when rows are plentiful and pieces few; otherwise a
     // row spreads over several workgroups: 32 columns each with 16-byte
@@ -817,7 +832,7 @@ hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_
         const dim3 block(64 * CMBW_ROWS);
         const int nv = (head_dim + 63) / 64;
 #define FD_CMBW(NV_) hipLaunchKernelGGL(lse_combine_rows_kernel<NV_>, grid, block, 0, stream, o_part, lse_part, \
-                                        rows, n_parts, head_dim, out, out_bf16, lse_out)
+                                        rows, n_parts, head_dim, out, orows, out_bf16, lse_out)
         if (nv <= 1) FD_CMBW(1);
         else if (nv == 2) FD_CMBW(2);
         else if (nv <= 4) FD_CMBW(4);
@@ -829,12 +844,12 @@ hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_
     if (vec4) {
         const dim3 grid4((unsigned)rows, (unsigned)((head_dim / 4 + CMB4_CV - 1) / CMB4_CV));
         hipLaunchKernelGGL(lse_combine_v4_kernel, grid4, dim3(256), 0, stream, o_part, lse_part, n_parts, head_dim,
-                           out, out_bf16, lse_out);
+                           out, orows, out_bf16, lse_out);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)rows, (unsigned)((head_dim + CMB_SLICE - 1) / CMB_SLICE));
     hipLaunchKernelGGL(lse_combine_kernel<1>, grid, dim3(CMB_THREADS), 0, stream, o_part, lse_part,
-                           n_parts, head_dim, out, out_bf16, lse_out);
+                           n_parts, head_dim, out, orows, out_bf16, lse_out);
     return hipGetLastError();
 }
 

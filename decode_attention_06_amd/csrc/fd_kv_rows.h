@@ -37,7 +37,7 @@ __device__ __forceinline__ int64_t kv_row_offset(const PartialParams& p, int b, 
     if constexpr (PAGED) {
         return kv_page_offset<D>(p, kv_page_id(p, b, t), kvh, t);
     } else {
-        return (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + (int64_t)t * D;
+        return (int64_t)b * p.kv_stride_b + (int64_t)kvh * p.kv_stride_h + (int64_t)t * p.kv_stride_t;
     }
 }
 

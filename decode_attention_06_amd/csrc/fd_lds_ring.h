@@ -47,7 +47,9 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * 256 + ((c ^ sw
 // non-temporal hint measured slower on both (bifurcated 1-3%, prefill
 // 2-11%).
 // Addresses are a wave-uniform base (row min(t0, c1 - 1)) plus a 32-bit
-// lane offset below 8 KiB, shared by K and V.  Four vector-memory
+// lane offset below 32 row strides (`st` elements from one row to the next;
+// the host keeps it below 2^24, so a 24-bit multiply forms it), shared by K
+// and V.  Four vector-memory
 // instructions per wave.
 // Offset registers of one wave's loads for a tile (one per KiB per
 // operand: 4 waves use both, 8 waves the first).
@@ -56,13 +58,13 @@ struct TileAddrs {
 };
 
 template <int NW>
-__device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uint16_t* vbase, int t0, int c1,
+__device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uint16_t* vbase, int st, int t0, int c1,
                                                     int wave, int lane, char* kst, char* vst) {
     typedef __attribute__((address_space(3))) void* lds_ptr;
     constexpr int IPW = 8 / NW;             // 1 KiB loads per wave per operand
     const int tbase = min(t0, c1 - 1);
-    const uint16_t* kt = kbase + (int64_t)tbase * MF_D;
-    const uint16_t* vt = vbase + (int64_t)tbase * MF_D;
+    const uint16_t* kt = kbase + (int64_t)tbase * st;
+    const uint16_t* vt = vbase + (int64_t)tbase * st;
     TileAddrs a;
 #pragma unroll
     for (int k = 0; k < IPW; ++k) {
@@ -70,7 +72,7 @@ __device__ __forceinline__ TileAddrs issue_tile(const uint16_t* kbase, const uin
         const int chunk = (lane & 15) ^ swz(row);
         const int t = min(t0 + row, c1 - 1);
         const int base = 1024 * (IPW * wave + k);
-        a.off[k] = (uint32_t)((t - tbase) * MF_D + 8 * chunk);
+        a.off[k] = __umul24((uint32_t)(t - tbase), (uint32_t)st) + 8 * chunk;
         __builtin_amdgcn_global_load_lds(kt + a.off[k], (lds_ptr)(kst + base), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vt + a.off[k], (lds_ptr)(vst + base), 16, 0, 0);
     }
@@ -117,11 +119,11 @@ __device__ __forceinline__ u32x4_t v_operand(const char* __restrict__ rv, int e,
 // qualifiers state that the stages are disjoint, which lets the compiler
 // read one stage while the other is still being filled.
 template <int NW>
-__device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint16_t* vbase, int t_issue, int c1,
+__device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint16_t* vbase, int st, int t_issue, int c1,
                                                    int wave, int lane, char* __restrict__ wk, char* __restrict__ wv,
                                                    const char* __restrict__ rk, const char* __restrict__ rv, int ktok0,
                                                    int g, int i, u32x4_t (&kr)[2][4], u32x4_t (&vt)[8]) {
-    const TileAddrs a = issue_tile<NW>(kbase, vbase, t_issue, c1, wave, lane, wk, wv);
+    const TileAddrs a = issue_tile<NW>(kbase, vbase, st, t_issue, c1, wave, lane, wk, wv);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int tt = ktok0 + 4 * blk;
@@ -141,8 +143,8 @@ __device__ __forceinline__ void ring_tile(const u32x4_t (&kr)[2][4], const u32x4
                                           float sl2, float (&m)[2], f32x4_t (&lacc)[2], f32x4_t (&acc)[2][8]) {
     f32x4_t sc[2][2];
     tile_scores<2>(kr, qb, sc);
-    bf16x8_t pb[2];
-    tile_softmax<2>(sc, tb, tmask, lim, g, sl2, m, lacc, acc, pb);
+    bf16x8_t pb[2], unused[2];
+    tile_softmax<2, false, f32x4_t>(sc, tb, tmask, lim, g, sl2, m, lacc, acc, pb, unused);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll

@@ -39,19 +39,21 @@
 namespace fd {
 namespace {
 
-template <int NRB, int NW, bool PAGED, bool KV8>
+template <int NRB, int NW, bool PAGED, bool KV8, bool PACK>
 __global__ __launch_bounds__(64 * NW, (NRB == 1 && NW == 4) ? 2 : 1) void partial_mfma_kernel(const PartialParams p) {
     static_assert(NW * MF_TILE == MFMA_TILE_ROWS, "workgroup step as the host computes it");
     __shared__ PartialLds<NRB, NW> sh;
-    partial_mfma_body<NRB, NW, PAGED, KV8>(p, blockIdx.x, sh);
+    partial_mfma_body<NRB, NW, PAGED, KV8, PACK>(p, blockIdx.x, sh);
 }
 
 template <bool PAGED, bool KV8>
 hipError_t launch_mfma_layout(const PartialParams& p, dim3 grid, int rows, hipStream_t stream) {
-    if (rows == 16) {
-        hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED, KV8>), grid, dim3(256), 0, stream, p);
+    if (rows == 16 && p.Hq / p.Hkv <= 8) {
+        hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED, KV8, true>), grid, dim3(256), 0, stream, p);
+    } else if (rows == 16) {
+        hipLaunchKernelGGL((partial_mfma_kernel<1, 4, PAGED, KV8, false>), grid, dim3(256), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((partial_mfma_kernel<2, 4, PAGED, KV8>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((partial_mfma_kernel<2, 4, PAGED, KV8, false>), grid, dim3(256), 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -65,6 +67,7 @@ hipError_t launch_partial_mfma(const PartialParams& p, bool fp8_cache, hipStream
     const int rows = mfma_rows_per_block(G);
     if (p.row_blocks != (G + rows - 1) / rows) return hipErrorInvalidValue;
     const int64_t units = (int64_t)p.B * p.Hkv * p.row_blocks;
+    if (units * p.n_splits >= (int64_t(1) << 30)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(units * p.n_splits));
     if (fp8_cache)
         return p.block_table ? launch_mfma_layout<true, true>(p, grid, rows, stream)

@@ -67,12 +67,23 @@ __device__ __forceinline__ u32x4_t block_column(const u32x4_t (&r)[8]) {
     return c;
 }
 
+// Output block E of O^T += V^T P^T for weights given as two bf16 parts,
+// pb (rounded weight) and pl (rounded remainder): two products per block.
 template <int E, int NRB>
 __device__ __forceinline__ void pv_block(const u32x4_t (&vr)[8], const bf16x8_t (&pb)[NRB],
-                                         f32x4_t (&acc)[NRB][8]) {
+                                         const bf16x8_t (&pl)[NRB], f32x4_t (&acc)[NRB][8]) {
     const bf16x8_t va = as_bf16x8(block_column<E>(vr));
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], acc[r][E], 0, 0, 0);
+    for (int r = 0; r < NRB; ++r) {
+        acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], acc[r][E], 0, 0, 0);
+        acc[r][E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[r], acc[r][E], 0, 0, 0);
+    }
+}
+
+// Output block E for one B operand holding both weight parts (PACK below).
+template <int E>
+__device__ __forceinline__ void pv_packed(const u32x4_t (&vr)[8], const bf16x8_t& pp, f32x4_t (&acc)[8]) {
+    acc[E] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(block_column<E>(vr)), pp, acc[E], 0, 0, 0);
 }
 
 // One 32-token tile of the online softmax for NRB blocks of 16 query rows,
@@ -106,10 +117,27 @@ __device__ __forceinline__ void tile_scores(const u32x4_t (&kr)[2][4], const bf1
 
 // tmask (wave-uniform): no token below it is masked for any row of the
 // wave; lim[r]: the lane's row of block r sees tokens below lim[r] only.
-template <int NRB>
+//
+// SPLIT: each fp32 weight w leaves as two bf16 values, pb = bf16(w) and
+// pl = bf16(w - pb) (w - pb is exact in fp32).  pb + pl is within
+// 2^-17 |w| of w, so the weights the products see are fp32-accurate and the
+// output error no longer grows with the spread of V (one bf16 weight is off
+// by up to 2^-9 |w|: about 2^-9 |v1 - v2| at the output).  The running sum
+// then takes the fp32 weights themselves: `lsum` (a float per row) holds the
+// sum over this lane's tokens only, and the caller adds the four lane
+// groups of a row at the end.  Without SPLIT, `lsum` is an f32x4 whose
+// every component holds the whole row's sum of the bf16 weights (a matrix
+// product against a block of ones), so numerator and denominator use
+// identical weights.  SPLIT doubles the P.V products, which the HBM-bound
+// split-KV kernels have to spare; the kernels whose matrix cores are the
+// bottleneck (many query rows per KV tile) keep one bf16 weight.
+//
+// PACK (see compute_tile): accumulator columns 8..15 hold the remainder
+// shares of rows 0..7, so a rescale applies row i's factor to column i + 8.
+template <int NRB, bool SPLIT, typename SumT, bool PACK = false>
 __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb, int tmask, const int (&lim)[NRB],
-                                             int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
-                                             f32x4_t (&acc)[NRB][8], bf16x8_t (&pb)[NRB]) {
+                                             int g, float sl2, float (&m)[NRB], SumT (&lsum)[NRB],
+                                             f32x4_t (&acc)[NRB][8], bf16x8_t (&pb)[NRB], bf16x8_t (&pl)[NRB]) {
     // A block of bf16 ones: O^T rows of ones(16 x 32) P^T give the row sums of
     // the very weights used in P V, accumulated in fp32 by the matrix core.
     const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -152,50 +180,118 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
             x = fmaxf(x, __shfl_xor(x, 32));
             const float mn = fmaxf(m[r], x * sl2);
             const float alpha = fast_exp2(m[r] - ((mn == -INFINITY) ? 0.f : mn));
-            lacc[r] *= alpha;
+            lsum[r] *= alpha;
+            float acc_alpha = alpha;
+            if constexpr (PACK) {
+                // row_shr:8 into banks 2 and 3: lane i + 8 of a 16-lane row
+                // takes lane i's factor, lanes 0..7 keep their own
+                acc_alpha = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(alpha), __float_as_int(alpha),
+                                                                        0x118, 0xF, 0xC, false));
+            }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+            for (int e = 0; e < 8; ++e) acc[r][e] *= acc_alpha;
             m[r] = mn;
         }
     }
-    // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix products.
+    // Weights exp2(s * sl2 - ref), rounded to bf16 for the matrix products
+    // (with SPLIT, the rounded remainder as well).
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         const float ref = (m[r] == -INFINITY) ? 0.f : m[r];
+        if constexpr (SPLIT) {
+            // pb: w cut to its top 16 bits (a bf16 value, exact as a float);
+            // pl: the exact remainder w - pb rounded to bf16.  Both parts
+            // together are within 2^-17 w of w.
+            u32x4_t hw, lw;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            bf16x2_t w2;
-            w2.x = (__bf16)fast_exp2(fmaf(t[r][j], sl2, -ref));
-            w2.y = (__bf16)fast_exp2(fmaf(t[r][j + 1], sl2, -ref));
-            pb[r][j] = w2.x;
-            pb[r][j + 1] = w2.y;
+            for (int j = 0; j < 8; j += 2) {
+                const float w0 = fast_exp2(fmaf(t[r][j], sl2, -ref));
+                const float w1 = fast_exp2(fmaf(t[r][j + 1], sl2, -ref));
+                const uint32_t u0 = __float_as_uint(w0), u1 = __float_as_uint(w1);
+                hw[j >> 1] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // top halves of w0, w1
+                bf16x2_t r2;
+                r2.x = (__bf16)(w0 - __uint_as_float(u0 & 0xffff0000u));
+                r2.y = (__bf16)(w1 - __uint_as_float(u1 & 0xffff0000u));
+                lw[j >> 1] = __builtin_bit_cast(uint32_t, r2);
+                lsum[r] += w0 + w1;
+            }
+            pb[r] = __builtin_bit_cast(bf16x8_t, hw);
+            pl[r] = __builtin_bit_cast(bf16x8_t, lw);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                bf16x2_t w2;
+                w2.x = (__bf16)fast_exp2(fmaf(t[r][j], sl2, -ref));
+                w2.y = (__bf16)fast_exp2(fmaf(t[r][j + 1], sl2, -ref));
+                pb[r][j] = w2.x;
+                pb[r][j + 1] = w2.y;
+            }
+            lsum[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[r], lsum[r], 0, 0, 0);
         }
-        lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[r], lacc[r], 0, 0, 0);
     }
 }
 
 // Whole tile with V held as the lane's 8x8 block (tokens 8g .. 8g+7,
 // d = 8i .. 8i+7), transposed in registers: output row m of block e is
-// d = 8m + e.
-template <int NRB>
+// d = 8m + e.  Split-KV kernels: weights in two bf16 parts (SPLIT above).
+//
+// PACK (one 16-row block holding at most 8 query rows, G <= 8): the
+// B-operand columns of the padding rows 8..15 carry the remainders of rows
+// 0..7 instead (moved over by 8 lanes within each 16-lane DPP row), so one
+// product per output block takes both parts; column i + 8 of the result
+// then holds row i's remainder share, which pack_fold() adds back once per
+// piece.
+template <int NRB, bool PACK = false>
 __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
                                              const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
-                                             float (&m)[NRB], f32x4_t (&lacc)[NRB], f32x4_t (&acc)[NRB][8]) {
+                                             float (&m)[NRB], float (&lsum)[NRB], f32x4_t (&acc)[NRB][8]) {
+    static_assert(!PACK || NRB == 1, "packing needs one block with spare columns");
     f32x4_t sc[NRB][2];
     tile_scores<NRB>(kr, qb, sc);
-    bf16x8_t pb[NRB];
+    bf16x8_t pb[NRB], pl[NRB];
     int lim[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) lim[r] = t1;
-    tile_softmax<NRB>(sc, tb, t1, lim, g, sl2, m, lacc, acc, pb);
-    pv_block<0>(vr, pb, acc);
-    pv_block<1>(vr, pb, acc);
-    pv_block<2>(vr, pb, acc);
-    pv_block<3>(vr, pb, acc);
-    pv_block<4>(vr, pb, acc);
-    pv_block<5>(vr, pb, acc);
-    pv_block<6>(vr, pb, acc);
-    pv_block<7>(vr, pb, acc);
+    tile_softmax<NRB, true, float, PACK>(sc, tb, t1, lim, g, sl2, m, lsum, acc, pb, pl);
+    if constexpr (PACK) {
+        const u32x4_t hi = __builtin_bit_cast(u32x4_t, pb[0]);
+        const u32x4_t lo = __builtin_bit_cast(u32x4_t, pl[0]);
+        u32x4_t pk;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // row_shr:8 written to banks 2 and 3 only (lanes 8..15 of each
+            // 16-lane row take lane i's remainder); lanes 0..7 keep pb
+            pk[k] = (uint32_t)__builtin_amdgcn_update_dpp((int)hi[k], (int)lo[k], 0x118, 0xF, 0xC, false);
+        }
+        const bf16x8_t pp = __builtin_bit_cast(bf16x8_t, pk);
+        pv_packed<0>(vr, pp, acc[0]);
+        pv_packed<1>(vr, pp, acc[0]);
+        pv_packed<2>(vr, pp, acc[0]);
+        pv_packed<3>(vr, pp, acc[0]);
+        pv_packed<4>(vr, pp, acc[0]);
+        pv_packed<5>(vr, pp, acc[0]);
+        pv_packed<6>(vr, pp, acc[0]);
+        pv_packed<7>(vr, pp, acc[0]);
+        return;
+    }
+    pv_block<0>(vr, pb, pl, acc);
+    pv_block<1>(vr, pb, pl, acc);
+    pv_block<2>(vr, pb, pl, acc);
+    pv_block<3>(vr, pb, pl, acc);
+    pv_block<4>(vr, pb, pl, acc);
+    pv_block<5>(vr, pb, pl, acc);
+    pv_block<6>(vr, pb, pl, acc);
+    pv_block<7>(vr, pb, pl, acc);
+}
+
+// PACK: adds column i + 8 of every accumulator (row i's remainder share)
+// into column i (row_shl:8 -- lane i of a 16-lane row reads lane i + 8).
+// Columns 8..15 are meaningless afterwards.
+__device__ __forceinline__ void pack_fold(f32x4_t (&acc)[1][8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[0][e][ii] += dpp<0x108>(acc[0][e][ii]);
 }
 
 }  // namespace

@@ -40,50 +40,68 @@ struct Fp8Tile {
 // unconditionally; a row index at or beyond t1 is clamped to t1 - 1, a valid
 // row whose score is masked to -inf later, so no row past the sequence
 // length is ever read.  `kb`, `vb`: element offsets from the pool to row 0
-// of the lane's K and V rows (dense: the (b, kvh) slice; paged: per group).
+// of the lane's K and V rows (dense: the (b, kvh) slice; paged: per group);
+// `st`: elements from one row to the next, below 2^24.  Addresses are a
+// wave-uniform base at row tbase = min(tb, last) plus a 32-bit lane offset
+// of dt = min(tb - tbase + token, last - tbase) rows (0 <= dt <= 31), formed
+// with a 24-bit multiply: row tbase + dt = min(tb + token, last), also for
+// a paged prefetch whose tile starts past the last row (tb > last).
+struct RowWindow {
+    int tbase, shift, lim;   // wave-uniform: base row, tb - tbase, last - tbase (both >= 0)
+};
+
+__device__ __forceinline__ RowWindow row_window(int tb, int last) {
+    const int tbase = min(tb, last);
+    return RowWindow{tbase, tb - tbase, last - tbase};
+}
+
+__device__ __forceinline__ uint32_t row_off(const RowWindow& w, int token, uint32_t st32) {
+    return __umul24((uint32_t)min(w.shift + token, w.lim), st32);
+}
+
 __device__ __forceinline__ void load_rows(const uint16_t* kpool, const uint16_t* vpool, int64_t ko, int64_t vo,
-                                          int tb, int last, int ktok0, int g, int i, Bf16Tile& r) {
+                                          int64_t st, int tb, int last, int ktok0, int g, int i, Bf16Tile& r) {
+    const RowWindow w = row_window(tb, last);
+    const uint16_t* kt = kpool + ko + (int64_t)w.tbase * st;
+    const uint16_t* vt = vpool + vo + (int64_t)w.tbase * st;
+    const uint32_t st32 = (uint32_t)st;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int t = min(tb + ktok0 + 4 * blk, last);
-        const uint16_t* src = kpool + ko + (int64_t)t * MF_D + 8 * g;
+        const uint32_t off = row_off(w, ktok0 + 4 * blk, st32) + 8u * (uint32_t)g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16_kv(src + 32 * s);
+        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16_kv(kt + off + 32 * s);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int t = min(tb + 8 * g + j, last);
-        r.v[j] = ld16_kv(vpool + vo + (int64_t)t * MF_D + 8 * i);
-    }
+    for (int j = 0; j < 8; ++j) r.v[j] = ld16_kv(vt + (row_off(w, 8 * g + j, st32) + 8u * (uint32_t)i));
 }
 
 __device__ __forceinline__ void load_rows(const uint8_t* kpool, const uint8_t* vpool, int64_t ko, int64_t vo,
-                                          int tb, int last, int ktok0, int g, int i, Fp8Tile& r) {
+                                          int64_t st, int tb, int last, int ktok0, int g, int i, Fp8Tile& r) {
+    const RowWindow w = row_window(tb, last);
+    const uint8_t* kt = kpool + ko + (int64_t)w.tbase * st;
+    const uint8_t* vt = vpool + vo + (int64_t)w.tbase * st;
+    const uint32_t st32 = (uint32_t)st;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int t = min(tb + ktok0 + 4 * blk, last);
-        const uint8_t* src = kpool + ko + (int64_t)t * MF_D + 32 * g;
-        r.k[blk][0] = ld16_kv(src);
-        r.k[blk][1] = ld16_kv(src + 16);
+        const uint32_t off = row_off(w, ktok0 + 4 * blk, st32) + 32u * (uint32_t)g;
+        r.k[blk][0] = ld16_kv(kt + off);
+        r.k[blk][1] = ld16_kv(kt + off + 16);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int t = min(tb + 8 * g + j, last);
-        r.v[j] = ld8_kv(vpool + vo + (int64_t)t * MF_D + 8 * i);
-    }
+    for (int j = 0; j < 8; ++j) r.v[j] = ld8_kv(vt + (row_off(w, 8 * g + j, st32) + 8u * (uint32_t)i));
 }
 
 // Computes one loaded tile (see compute_tile).
-template <int NRB>
+template <int NRB, bool PACK>
 __device__ __forceinline__ void compute_loaded(const Bf16Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
-                                               int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
+                                               int g, float sl2, float (&m)[NRB], float (&lsum)[NRB],
                                                f32x4_t (&acc)[NRB][8]) {
-    compute_tile<NRB>(r.k, r.v, qb, tb, t1, g, sl2, m, lacc, acc);
+    compute_tile<NRB, PACK>(r.k, r.v, qb, tb, t1, g, sl2, m, lsum, acc);
 }
 
-template <int NRB>
+template <int NRB, bool PACK>
 __device__ __forceinline__ void compute_loaded(const Fp8Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
-                                               int g, float sl2, float (&m)[NRB], f32x4_t (&lacc)[NRB],
+                                               int g, float sl2, float (&m)[NRB], float (&lsum)[NRB],
                                                f32x4_t (&acc)[NRB][8]) {
     u32x4_t kr[2][4], vr[8];
 #pragma unroll
@@ -96,7 +114,7 @@ __device__ __forceinline__ void compute_loaded(const Fp8Tile& r, const bf16x8_t 
         }
 #pragma unroll
     for (int j = 0; j < 8; ++j) vr[j] = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
-    compute_tile<NRB>(kr, vr, qb, tb, t1, g, sl2, m, lacc, acc);
+    compute_tile<NRB, PACK>(kr, vr, qb, tb, t1, g, sl2, m, lsum, acc);
 }
 
 // Paged tiles.  A tile (16-row aligned) covers two 16-row groups, each
@@ -136,7 +154,9 @@ struct PartialLds {
     float l[NW][ROWS];
 };
 
-template <int NRB, int NW, bool PAGED = false, bool KV8 = false>
+// PACK: at most 8 query rows per unit (G <= 8, one 16-row block); the
+// weights' remainders ride in the block's padding columns (compute_tile).
+template <int NRB, int NW, bool PAGED = false, bool KV8 = false, bool PACK = false>
 __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bid, PartialLds<NRB, NW>& sh) {
     using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
     using Tile = typename std::conditional<KV8, Fp8Tile, Bf16Tile>::type;
@@ -192,7 +212,9 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         for (int s = 0; s < 4; ++s) {
             u32x4_t v = {0u, 0u, 0u, 0u};
             const int d0 = KV8 ? 32 * g + 8 * s : 32 * s + 8 * g;
-            if (row < nr) v = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h0 + row) * D + d0);
+            if (row < nr)
+                v = ld16(static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_stride_b +
+                         (int64_t)(h0 + row) * p.q_stride_h + d0);
             qb[r][s] = as_bf16x8(v);
         }
     }
@@ -207,12 +229,12 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     const float sl2 = p.scale_log2 * (p.k_scale ? p.k_scale[kvh] : 1.f);
     const float vsc = p.v_scale ? p.v_scale[kvh] : 1.f;
 
-    f32x4_t acc[NRB][8], lacc[NRB];
-    float m[NRB];
+    f32x4_t acc[NRB][8];
+    float m[NRB], lsum[NRB];   // lsum: this lane's share of its row's running sum
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         m[r] = -INFINITY;
-        lacc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lsum[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -237,11 +259,11 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
             // then sits at offset + t * D).
             const int64_t o0 = kv_page_offset<MF_D>(p, ahead.id0, kvh, ahead.s0) - (int64_t)ahead.s0 * MF_D;
             const int64_t o1 = kv_page_offset<MF_D>(p, ahead.id1, kvh, ahead.s1) - (int64_t)ahead.s1 * MF_D;
-            load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, at, t1 - 1, ktok0, g, i, r);
+            load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, (int64_t)MF_D, at, t1 - 1, ktok0, g, i, r);
             ahead = ahead2;
             ahead2 = paged_tile(p, b, at + 2 * step, t1 - 1);
         } else {
-            load_rows(kpool, vpool, slice, slice, at, t1 - 1, ktok0, g, i, r);
+            load_rows(kpool, vpool, slice, slice, p.kv_stride_t, at, t1 - 1, ktok0, g, i, r);
         }
     };
     int tb = t0 + wave * MF_TILE;
@@ -253,34 +275,41 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         load(tb, ta);
         while (true) {
             if (!PAGED && tb + step >= t1) {
-                compute_loaded<NRB>(ta, qb, tb, t1, g, sl2, m, lacc, acc);
+                compute_loaded<NRB, PACK>(ta, qb, tb, t1, g, sl2, m, lsum, acc);
                 break;
             }
             load(tb + step, tn);
-            compute_loaded<NRB>(ta, qb, tb, t1, g, sl2, m, lacc, acc);
+            compute_loaded<NRB, PACK>(ta, qb, tb, t1, g, sl2, m, lsum, acc);
             tb += step;
             if (PAGED && tb >= t1) break;
             if (!PAGED && tb + step >= t1) {
-                compute_loaded<NRB>(tn, qb, tb, t1, g, sl2, m, lacc, acc);
+                compute_loaded<NRB, PACK>(tn, qb, tb, t1, g, sl2, m, lsum, acc);
                 break;
             }
             load(tb + step, ta);
-            compute_loaded<NRB>(tn, qb, tb, t1, g, sl2, m, lacc, acc);
+            compute_loaded<NRB, PACK>(tn, qb, tb, t1, g, sl2, m, lsum, acc);
             tb += step;
             if (PAGED && tb >= t1) break;
         }
     }
 
-    // Merge of the waves' states (row sums already complete in lacc).
+    // Merge of the waves' states.  A row's running sum is first completed
+    // over its four lane groups (every lane of the row then holds it).
     // Every lane computes its rows' merged max M and sum L from the waves'
     // (m, l) and scales its own accumulators by exp2(m - M) / L in
     // registers; what is left per output element is a plain sum over waves.
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
+        lsum[r] += __shfl_xor(lsum[r], 16);
+        lsum[r] += __shfl_xor(lsum[r], 32);
+    }
+    if constexpr (PACK) pack_fold(acc);
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
         const int row = r * 16 + i;
         if (g == 0 && row < nr) {
             s_m[wave][row] = m[r];
-            s_l[wave][row] = lacc[r][0];
+            s_l[wave][row] = lsum[r];
         }
     }
     __syncthreads();
@@ -332,7 +361,7 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
         for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4_t*>(&s_acc[w][row][d0]);
         const int64_t orow = (int64_t)b * p.Hq + h0 + row;
         if (p.direct) {
-            const int64_t o0 = orow * D + d0;
+            const int64_t o0 = (int64_t)b * p.out_stride_b + (int64_t)(h0 + row) * p.out_stride_h + d0;
             if (p.out_bf16 && vec_bf16) {
                 const uint32_t lo = (uint32_t)to_bf16(a[0]) | ((uint32_t)to_bf16(a[1]) << 16);
                 const uint32_t hi = (uint32_t)to_bf16(a[2]) | ((uint32_t)to_bf16(a[3]) << 16);

@@ -109,10 +109,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // order): the first wait below covers them too.
     u32x4_t kr[2][4], vt[8];
 #pragma unroll
-    for (int t = 0; t < CTX_STAGES - 1; ++t) issue_tile<PF_NW>(kbase, vbase, t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
+    for (int t = 0; t < CTX_STAGES - 1; ++t) issue_tile<PF_NW>(kbase, vbase, MF_D, t * CTX_TILE, c1, wave, lane, ks[t], vs[t]);
     wait_vm<TWO_TILES>();
     ring_barrier();
-    const TileAddrs a0 = ring_step<PF_NW>(kbase, vbase, (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
+    const TileAddrs a0 = ring_step<PF_NW>(kbase, vbase, MF_D, (CTX_STAGES - 1) * CTX_TILE, c1, wave, lane,
                                           ks[CTX_STAGES - 1], vs[CTX_STAGES - 1], ks[0], vs[0], ktok0, g, i, kr, vt);
     keep_addrs<PF_NW>(a0);
     for (int t4 = 0; t4 < n_tiles; t4 += CTX_STAGES) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
             if (t + 1 >= n_tiles) break;
             wait_vm<TWO_TILES>();
             ring_barrier();
-            const TileAddrs an = ring_step<PF_NW>(kbase, vbase, (t + CTX_STAGES) * CTX_TILE, c1, wave, lane, ks[st],
+            const TileAddrs an = ring_step<PF_NW>(kbase, vbase, MF_D, (t + CTX_STAGES) * CTX_TILE, c1, wave, lane, ks[st],
                                                   vs[st], ks[(st + 1) % CTX_STAGES], vs[(st + 1) % CTX_STAGES], ktok0, g,
                                                   i, kr, vt);
             keep_addrs<PF_NW>(an);

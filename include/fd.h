@@ -32,7 +32,8 @@
  *    the stream; work is enqueued on `stream` (a hipStream_t, NULL = the
  *    default stream) and faults inside kernels surface at the caller's next
  *    synchronisation.
- *  - Tensors are dense and row-major, last index fastest:
+ *  - Tensors are dense and row-major, last index fastest (the *_strided
+ *    entry points take fd_tensor descriptors with strides instead):
  *        q    [B, Hq, D]            (bifurcated: [S, Hq, D])
  *        k, v [B, Hkv, Lmax, D]     (context: [Hkv, Lc, D];
  *                                    decode: [S, Hkv, Ldmax, D])
@@ -46,8 +47,9 @@
  *    FD_ERR_UNSUPPORTED; there is no silent fallback.
  *  - Every shape, pointer, alignment and workspace check runs before the
  *    first HIP call; a failing check returns its status and leaves the
- *    stream untouched.  Device-resident lengths cannot be checked without a
- *    synchronisation and are preconditions.
+ *    stream untouched.  Device-resident lengths and block tables cannot be
+ *    checked without a synchronisation and are preconditions, checked only
+ *    when validation is on (fd_set_validation, FD_VALIDATE=1).
  *  - Errors are returned as fd_status; fd_last_error_message() gives a
  *    thread-local description of the most recent failure.  No entry point
  *    aborts or throws.
@@ -80,6 +82,22 @@ typedef enum fd_dtype {
      * fd_decode_attn_workspace_size. */
     FD_FP8_E4M3 = 2
 } fd_dtype;
+
+/* A tensor passed by descriptor (the *_strided entry points): a device
+ * pointer, its element type (fd_dtype), and `ndim` dimensions in the
+ * logical order the entry point names, outermost first, with the element
+ * stride of each.  The last dimension (the head dim) must be contiguous
+ * (stride 1); every other stride must be >= 0 and a multiple of 16 bytes,
+ * and data 16-byte aligned.  A token-major cache [B, L, Hkv, D] is passed as
+ * the logical [B, Hkv, L, D] with strides {L*Hkv*D, D, Hkv*D, 1}.  Unused
+ * shape / stride entries are ignored. */
+typedef struct fd_tensor {
+    void* data;
+    int32_t dtype;
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} fd_tensor;
 
 /* Largest split count accepted (per sequence for decode; context plus
  * decode pieces for the bifurcated call). */
@@ -199,6 +217,30 @@ fd_status fd_decode_attn_noalloc(const void* q, const void* k, const void* v, co
                                  void* out, int32_t out_dtype, float* lse_out, float scale, void* stream);
 
 /*
+ * fd_decode_attn_strided - fd_decode_attn (or, for an E4M3 cache,
+ * fd_decode_attn_fp8) on tensors given by descriptors with arbitrary
+ * strides, so that views and other cache layouts (token-major, a slice of a
+ * larger pool) need no copy ([FA] "Il supporto hardware e la forma dei dati
+ * determinano l'uso del percorso rapido": a fast path states exactly which
+ * layouts it takes and checks them).
+ *
+ *   q    logical [B, Hq, D], dtype FD_F32 / FD_BF16 (FD_BF16 for an E4M3 cache)
+ *   k, v logical [B, Hkv, Lmax, D], the same shape, strides and dtype
+ *        (FD_F32, FD_BF16 or FD_FP8_E4M3); the token stride below 2^24
+ *        elements and at most 2^27 bytes
+ *   k_scale, v_scale  E4M3 cache only: as in fd_decode_attn_fp8
+ *   out  logical [B, Hq, D], FD_F32 or FD_BF16, rows must not overlap
+ *   everything else   as in fd_decode_attn; the workspace size is
+ *                     fd_decode_attn_workspace_size() of the same shapes
+ * Results equal fd_decode_attn's on the same values bit for bit, for the
+ * same n_splits.
+ */
+fd_status fd_decode_attn_strided(const fd_tensor* q, const fd_tensor* k, const fd_tensor* v, const float* k_scale,
+                                 const float* v_scale, const int32_t* lens, int32_t n_splits, const fd_tensor* out,
+                                 float* lse_out, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * fd_decode_attn_fp8 - fd_decode_attn over a KV cache of 8-bit floating
  * point codes ([MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", quantisation
  * paragraph: fewer bits per stored value, fewer bytes over the memory bus).
@@ -310,6 +352,50 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
                              void* stream);
 
 /*
+ * fd_bifurcated_attn_paged - fd_bifurcated_attn with each sample's decode
+ * rows in a paged pool ([MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ",
+ * PagedAttention paragraph: fixed-size blocks found through an indirection
+ * table), as a serving cache keeps the rows every sample appends; the shared
+ * context stays dense.  The result equals fd_bifurcated_attn on the gathered
+ * decode cache bit for bit.
+ *
+ *   q, k_ctx, v_ctx, dec_lens, out, lse_out, scale: as in fd_bifurcated_attn
+ *   k_pages, v_pages   [num_pages, Hkv, page_size, D]
+ *   block_table        device int32 [S, max_pages_per_seq]: decode row t of
+ *                      sample s is row t % page_size of page
+ *                      block_table[s][t / page_size]; only entries covering
+ *                      rows < dec_lens[s] are read; ids outside
+ *                      [0, num_pages) are clamped into it
+ *   page_size, num_pages, max_pages_per_seq: as in fd_decode_attn_paged;
+ *                      Ldmax = max_pages_per_seq * page_size
+ *   workspace          fd_bifurcated_attn_workspace_size(..., Ldmax, ...)
+ */
+fd_status fd_bifurcated_attn_paged(const void* q, const void* k_ctx, const void* v_ctx, const void* k_pages,
+                                   const void* v_pages, const int32_t* block_table, const int32_t* dec_lens,
+                                   int32_t samples, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int64_t ctx_len, int32_t page_size, int64_t num_pages,
+                                   int32_t max_pages_per_seq, int32_t dtype, void* out, int32_t out_dtype,
+                                   float* lse_out, float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * fd_bifurcated_attn_strided - fd_bifurcated_attn on tensors given by
+ * descriptors (see fd_tensor and fd_decode_attn_strided).
+ *
+ *   q             logical [S, Hq, D]
+ *   k_ctx, v_ctx  logical [Hkv, Lc, D], the same shape, strides and dtype
+ *   k_dec, v_dec  logical [S, Hkv, Ldmax, D], the same shape, strides, dtype
+ *   out           logical [S, Hq, D], rows must not overlap
+ *   q and both caches share one dtype (FD_F32 or FD_BF16); token strides
+ *   below 2^24 elements and at most 2^27 bytes.  Everything else as in
+ *   fd_bifurcated_attn.
+ */
+fd_status fd_bifurcated_attn_strided(const fd_tensor* q, const fd_tensor* k_ctx, const fd_tensor* v_ctx,
+                                     const fd_tensor* k_dec, const fd_tensor* v_dec, const int32_t* dec_lens,
+                                     const fd_tensor* out, float* lse_out, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * fd_prefill_attn - causal many-query (prefill) attention over a whole
  * sequence ([FD] "Por qué la decodificación necesita otra planificación":
  * during prefill many query positions run in parallel; [MW] section on why
@@ -348,6 +434,21 @@ fd_status fd_prefill_attn(const void* q, const void* k, const void* v, const int
 fd_status fd_lse_combine(const float* o_part, const float* lse_part, int32_t rows,
                          int32_t n_parts, int32_t head_dim, void* out, int32_t out_dtype,
                          float* lse_out, void* stream);
+
+/*
+ * fd_set_validation - turn device-side argument validation on (1) or off
+ * (0) for every later call in the process; FD_VALIDATE=1 in the environment
+ * turns it on when the library is first used.  With validation on, each
+ * entry point first checks the device-resident arrays it is about to read
+ * (lens / dec_lens against their documented ranges, and the block-table
+ * entries that cover valid rows against [0, num_pages)), synchronises the
+ * stream, and returns FD_ERR_INVALID_ARG naming the first bad entry before
+ * any attention kernel runs.  It costs a synchronisation per call and
+ * returns FD_ERR_UNSUPPORTED under stream capture: a debugging aid.
+ * fd_validation_enabled() reports the current setting.
+ */
+fd_status fd_set_validation(int32_t on);
+int32_t fd_validation_enabled(void);
 
 /*
  * fd_read_probe - measurement aid, not part of the attention path: streams

@@ -8,6 +8,7 @@ from .fp64 import (  # noqa: F401
     attention,
     attention_fp8kv,
     bifurcated_attention,
+    bifurcated_paged_attention,
     default_scale,
     fp8_e4m3_value,
     lse_combine,

@@ -51,6 +51,7 @@ __all__ = [
     "default_scale",
     "attention",
     "bifurcated_attention",
+    "bifurcated_paged_attention",
     "split_partials",
     "lse_combine",
     "paged_attention",
@@ -304,6 +305,53 @@ def bifurcated_attention(q, k_ctx, v_ctx, k_dec, v_dec, dec_lens=None, scale=Non
             keys = np.concatenate([k_ctx[g], k_dec[s, g, :n]], axis=0)
             vals = np.concatenate([v_ctx[g], v_dec[s, g, :n]], axis=0)
             o, l = _attend_rows(q[s, rows], keys, vals, scale)
+            out[s, rows] = o
+            lse[s, rows] = l
+    return out, lse
+
+
+def bifurcated_paged_attention(q, k_ctx, v_ctx, k_pages, v_pages, block_table, dec_lens, scale=None):
+    """Bifurcated attention with each sample's decode rows in a paged pool.
+
+    q                 [S, Hq, D]
+    k_ctx, v_ctx      [Hkv, Lc, D]          shared context, dense
+    k_pages, v_pages  [n_pages, Hkv, P, D]  pages of P rows for each KV head
+    block_table       [S, max_pages] integer page ids
+    dec_lens          [S] integers in [0, max_pages * P]
+
+    [BA] "Tiivistelmä": sample s attends over [context rows ; its own decode
+    rows].  [MW] "ಮೆಮೊರಿ ವಾಲ್ (Memory Wall) ವಿರುದ್ಧ ಹೋರಾಟ", PagedAttention:
+    decode row t of sample s is row t mod P of page block_table[s, t div P];
+    only the entries covering rows below dec_lens[s] are read.
+    """
+    q = _as_f64(q)
+    k_ctx, v_ctx, k_pages, v_pages = map(_as_f64, (k_ctx, v_ctx, k_pages, v_pages))
+    S, Hq, D = q.shape
+    Hkv, Lc, _ = k_ctx.shape
+    n_pages, Hkp, P, _ = k_pages.shape
+    table = np.asarray(block_table, dtype=np.int64)
+    if Hkp != Hkv or v_pages.shape != k_pages.shape or table.shape[0] != S:
+        raise ValueError("shape mismatch between q, the context, the pages and the block table")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    dec_lens = np.asarray(dec_lens, dtype=np.int64)
+    if scale is None:
+        scale = default_scale(D)
+    out = np.empty((S, Hq, D))
+    lse = np.empty((S, Hq))
+    for s in range(S):
+        n = int(dec_lens[s])
+        if not 0 <= n <= table.shape[1] * P:
+            raise ValueError(f"dec_lens[{s}]={n} outside [0, {table.shape[1] * P}]")
+        pages = [int(table[s, t // P]) for t in range(n)]
+        if any(pg < 0 or pg >= n_pages for pg in pages):
+            raise ValueError(f"sample {s} names a page outside [0, {n_pages})")
+        for g in range(Hkv):
+            rows = slice(g * G, (g + 1) * G)
+            dk = np.array([k_pages[pages[t], g, t % P] for t in range(n)]).reshape(n, D)
+            dv = np.array([v_pages[pages[t], g, t % P] for t in range(n)]).reshape(n, D)
+            o, l = _attend_rows(q[s, rows], np.concatenate([k_ctx[g], dk]), np.concatenate([v_ctx[g], dv]), scale)
             out[s, rows] = o
             lse[s, rows] = l
     return out, lse

@@ -55,3 +55,46 @@ def sampled_units(w, count, seed):
     while len(units) < min(count, w.batch * w.kv_heads):
         units.add((int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))))
     return sorted(units)
+
+
+def check_every_unit(q, fetch_kv, lens_h, out, lse, tol, scale=None):
+    """Properties of exact attention checked on every output row of a
+    full-size call (the oracle covers sampled units one by one):
+
+    * every output element lies in the convex hull of its KV head's valid
+      value rows: min_j V[j, d] - tol <= out[d] <= max_j V[j, d] + tol;
+    * the lse lies between the largest scaled score and that plus ln(n):
+      max_j s_j - tol <= lse <= max_j s_j + ln(n) + tol.
+
+    q [B, Hq, D] and out [B, Hq, D], lse [B, Hq] are device tensors;
+    fetch_kv(b) returns sequence b's valid rows as fp32 device tensors
+    k, v [Hkv, n, D] (n = lens_h[b]).  The scores are formed in fp32 on the
+    device, one sequence at a time; they only bound the lse.  Returns the
+    number of rows checked.
+    """
+    B, Hq, D = q.shape
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    for b in range(B):
+        n = int(lens_h[b])
+        kb, vb = fetch_kv(b)
+        Hkv = kb.shape[0]
+        G = Hq // Hkv
+        assert kb.shape == (Hkv, n, D) and vb.shape == (Hkv, n, D)
+        qb = q[b].float().reshape(Hkv, G, D).transpose(1, 2).contiguous()   # [Hkv, D, G]
+        s = torch.matmul(kb.contiguous(), qb) * scale             # [Hkv, n, G]
+        smax = s.amax(dim=1).reshape(Hq)                          # [Hq]
+        lo = vb.amin(dim=1).repeat_interleave(G, dim=0)           # [Hq, D]
+        hi = vb.amax(dim=1).repeat_interleave(G, dim=0)
+        ob = out[b].float()
+        assert torch.isfinite(ob).all(), f"non-finite output in sequence {b}"
+        assert bool((ob >= lo - tol).all() and (ob <= hi + tol).all()), f"output outside the value hull, seq {b}"
+        lb = lse[b].float()
+        assert bool((lb >= smax - tol).all() and (lb <= smax + float(np.log(n)) + tol).all()), \
+            f"lse outside [max score, max score + ln n], seq {b}"
+        del kb, vb, s
+    return B * Hq
+
+
+def dense_rows(k, v, lens_h):
+    """fetch_kv for a dense cache [B, Hkv, L, D]."""
+    return lambda b: (k[b, :, :int(lens_h[b])].float(), v[b, :, :int(lens_h[b])].float())

@@ -14,7 +14,8 @@ AssertionError when the oracle disagrees with:
   bifurcated = split into context and decode pieces, GQA = MHA with repeated
   KV, row permutation, shift and linearity in V, convex hull, lse value;
 * paged = dense attention on a cache scattered into a shuffled, poisoned
-  page pool by an independently written inverse of the page layout;
+  page pool by an independently written inverse of the page layout, and
+  likewise bifurcated attention with paged decode rows = dense bifurcated;
 * E4M3 code values against torch's float8_e4m3fn decoder and hand-worked
   landmarks; fp8-cache attention = dense attention on the values that
   decoder gives, times the per-head scales;
@@ -337,6 +338,24 @@ def pin_paged_is_dense_attention(orc):
         _close(lse, ref_lse, 0.0, f"paged case {seed} lse")
 
 
+def pin_bifurcated_paged_is_dense_bifurcated(orc):
+    # [BA] "Tiivistelmä" with [MW] PagedAttention: paging every sample's
+    # decode rows only relocates them; the result is the dense bifurcated
+    # result on the same rows (empty decode parts included), and no poisoned
+    # row, page or table entry is read.
+    for seed, (S, Hq, Hkv, D, Lc, Ld, P) in enumerate([(4, 4, 2, 8, 13, 21, 4), (3, 2, 1, 5, 3, 16, 16),
+                                                       (5, 6, 3, 4, 7, 9, 1)]):
+        q = _rand((S, Hq, D), 190 + seed)
+        kc, vc = _rand((Hkv, Lc, D), 191 + seed), _rand((Hkv, Lc, D), 192 + seed)
+        kd, vd = _rand((S, Hkv, Ld, D), 193 + seed), _rand((S, Hkv, Ld, D), 194 + seed)
+        dl = np.array([Ld, 0, 1, Ld - 3, 5][:S])
+        kp, vp, table = scatter_to_pages(kd, vd, dl, P, extra_pages=2, seed=195 + seed)
+        out, lse = orc.bifurcated_paged_attention(q, kc, vc, kp, vp, table, dl, 0.4)
+        ref_out, ref_lse = orc.bifurcated_attention(q, kc, vc, kd, vd, dl, 0.4)
+        _close(out, ref_out, 0.0, f"bifurcated paged case {seed} out")
+        _close(lse, ref_lse, 0.0, f"bifurcated paged case {seed} lse")
+
+
 def pin_fp8_codes(orc):
     # every E4M3 code against torch's float8_e4m3fn (a library decoder) ...
     import torch
@@ -410,5 +429,6 @@ def pin_prefill(orc):
 
 ALL_PINS = [pin_golden, pin_decimal_bruteforce, pin_torch_sdpa, pin_closed_forms,
             pin_split_independence, pin_bifurcated_split, pin_gqa_is_repeated_mha,
-            pin_row_and_value_invariants, pin_paged_is_dense_attention, pin_fp8_codes,
+            pin_row_and_value_invariants, pin_paged_is_dense_attention, pin_bifurcated_paged_is_dense_bifurcated,
+            pin_fp8_codes,
             pin_fp8_attention_is_dense_attention, pin_prefill]

@@ -26,9 +26,13 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -331,3 +335,43 @@ def test_noalloc_checks_before_any_hip_call(lib):
     assert call(q=MISALIGNED) == fd.FD_ERR_INVALID_ARG
     assert call(B=0) == fd.FD_ERR_INVALID_ARG
     assert call(n_splits=fd.FD_MAX_SPLITS + 1) == fd.FD_ERR_INVALID_ARG
+
+
+def test_testing_entry_point_checks_before_any_hip_call(lib):
+    def call(kernel, dtype=fd.FD_BF16, D=128, q=FAKE):
+        return lib.fd_testing_decode_attn(q, FAKE, FAKE, None, None, None, 1, 8, 2, D, 512, dtype, 4, FAKE,
+                                          fd.FD_F32, None, 0.0, FAKE, 0, None, kernel)
+    assert call(3) == fd.FD_ERR_INVALID_ARG
+    assert call(2, dtype=fd.FD_F32) == fd.FD_ERR_UNSUPPORTED        # matrix-core kernel: bf16 / E4M3 only
+    assert call(2, D=64) == fd.FD_ERR_UNSUPPORTED
+    assert call(1, q=None) == fd.FD_ERR_INVALID_ARG
+    assert call(1) == fd.FD_ERR_WORKSPACE                           # 4 pieces need a workspace
+
+
+def test_decode_grid_limit_is_checked(lib):
+    # 2^22 sequences x 64 KV heads x 4 pieces = 2^30 work units: unsupported, before any launch
+    B = 1 << 22
+    assert _decode(lib, B=B, Hq=64, Hkv=64, n_splits=4, ws=FAKE, ws_bytes=1 << 62) == fd.FD_ERR_UNSUPPORTED
+    assert "2^30" in lib.fd_last_error_message().decode()
+    rc = lib.fd_decode_attn_partials(FAKE, FAKE, FAKE, None, B, 64, 64, 64, 512, fd.FD_F32, 4, 0, FAKE, FAKE,
+                                     0.0, None)
+    assert rc == fd.FD_ERR_UNSUPPORTED
+
+
+def test_planner_ignores_the_environment(lib, monkeypatch):
+    # the split count and the piece tile are functions of their arguments only
+    before = (fd.plan_splits(1, 16, 2, 128, 65536, fd.FD_BF16, 256), fd.piece_tile_rows(16, 2, 128, fd.FD_BF16))
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "valu")
+    after = (fd.plan_splits(1, 16, 2, 128, 65536, fd.FD_BF16, 256), fd.piece_tile_rows(16, 2, 128, fd.FD_BF16))
+    assert before == after == (128, 128)
+
+
+def test_validation_switch(lib, monkeypatch):
+    was = fd.validation_enabled()
+    try:
+        fd.set_validation(True)
+        assert fd.validation_enabled()
+        fd.set_validation(False)
+        assert not fd.validation_enabled()
+    finally:
+        fd.set_validation(was)

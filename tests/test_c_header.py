@@ -13,6 +13,7 @@ LIBDIR = os.path.join(ROOT, "decode_attention_06_amd", "lib")
 
 PROGRAM = r"""
 #include "fd.h"
+#include "fd_testing.h"
 #include <stdio.h>
 
 int main(void) {
@@ -29,6 +30,11 @@ int main(void) {
     st = fd_decode_attn(NULL, NULL, NULL, NULL, 1, 16, 2, 128, 65536, dt, 0, NULL, FD_BF16, NULL, 0.0f, NULL, 0, NULL);
     printf("null %s %d\n", fd_status_string(st), fd_last_error_message()[0] != '\0');
     printf("layout %d max %d\n", (int)lay, FD_MAX_SPLITS);
+    st = fd_testing_decode_attn(NULL, NULL, NULL, NULL, NULL, NULL, 1, 16, 2, 128, 512, dt, 4, NULL, FD_F32, NULL,
+                                0.0f, NULL, 0, NULL, 7);
+    printf("testing %s\n", fd_status_string(st));
+    st = fd_decode_attn_noalloc(NULL, NULL, NULL, NULL, 1, 16, 2, 128, 512, dt, 4, NULL, FD_F32, NULL, 0.0f, NULL);
+    printf("noalloc %s %u\n", fd_status_string(st), (unsigned)FD_NOALLOC_MAX_WORKSPACE);
     return 0;
 }
 """
@@ -58,3 +64,5 @@ def test_header_compiles_and_links(tmp_path, compiler, flags):
     assert st == "0" and int(ws) >= 16 * 128 * 129 * 4
     assert lines["null"] == "FD_ERR_INVALID_ARG 1"
     assert lines["layout"] == "1 max 4096"
+    assert lines["testing"] == "FD_ERR_INVALID_ARG"
+    assert lines["noalloc"] == "FD_ERR_INVALID_ARG 16777216"

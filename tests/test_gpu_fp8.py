@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_cases import max_abs, sampled_units, to_dev, to_host
+from tests.gpu_cases import check_every_unit, max_abs, sampled_units, to_dev, to_host
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -57,15 +57,21 @@ def test_fp8_matches_oracle(fd, shape, n_splits):
 
 
 @pytest.mark.parametrize("kernel", ["mfma", "valu"])
-def test_fp8_both_kernels_unit_scales_and_bf16_out(fd, kernel, monkeypatch):
+def test_fp8_both_kernels_unit_scales_and_bf16_out(fd, kernel):
     """Scales left NULL (= 1) and a bf16 output, through each partial kernel
-    (the choice of kernel is forced where both support the shape)."""
-    monkeypatch.setenv("FD_PARTIAL_KERNEL", kernel)
+    (the test entry point picks the kernel where both support the shape)."""
     case = synth.fp8_case(2, 16, 2, 128, 800, seed=4100, lens=[800, 333])
     case["k_bits"] = synth.to_e4m3(synth.host_normal((2, 2, 800, 128), 4101, "fp32") * 0.2, np.ones(2))
     case["v_bits"] = synth.to_e4m3(synth.host_normal((2, 2, 800, 128), 4102, "fp32"), np.ones(2))
+    q = to_dev(case["q"], "bf16")
+    k = torch.from_numpy(case["k_bits"]).to("cuda")
+    v = torch.from_numpy(case["v_bits"]).to("cuda")
+    lens = torch.from_numpy(case["lens"]).to("cuda")
     for ns in (0, 4):
-        out, lse = run_fp8(fd, case, ns, out_dtype=torch.bfloat16, scales=False)
+        o, l = fd.testing_decode_attn(q, k, v, kernel, lens=lens, n_splits=ns, out_dtype=torch.bfloat16,
+                                      return_lse=True)
+        torch.cuda.synchronize()
+        out, lse = to_host(o), to_host(l)
         ref_out, ref_lse = oracle.attention_fp8kv(case["q"], case["k_bits"], case["v_bits"], None, None,
                                                   case["lens"])
         assert max_abs(out, ref_out) <= TOL and max_abs(lse, ref_lse) <= TOL
@@ -83,11 +89,10 @@ def test_fp8_extreme_codes(fd):
     out, lse = run_fp8(fd, case, 0)
     ref_out, ref_lse = oracle.attention_fp8kv(case["q"], case["k_bits"], case["v_bits"], case["k_scale"],
                                               case["v_scale"], case["lens"])
-    # V values reach 448 * scale (about 6): bf16 weights carry at most 2^-9
-    # relative error, the same in numerator and denominator, so the output
-    # error stays below 2^-8 times the largest value magnitude.
-    vmax = float(np.nanmax(np.abs(oracle.fp8_e4m3_value(case["v_bits"]) * case["v_scale"][None, :, None, None])))
-    assert max_abs(out, ref_out) <= max(TOL, 2.0 ** -8 * vmax) and max_abs(lse, ref_lse) <= TOL
+    # V values reach 448 * scale (about 6).  The split-KV kernels pass each
+    # softmax weight to the matrix cores as two bf16 parts (fp32-accurate),
+    # so the flat bound holds whatever the spread of V.
+    assert max_abs(out, ref_out) <= TOL and max_abs(lse, ref_lse) <= TOL
 
 
 def make_fp8_workload(w):
@@ -128,5 +133,13 @@ def test_fp8_workload_full_size(fd, w):
         worst = max(worst, max_abs(out_h[b, g * G:(g + 1) * G], ro[0]), max_abs(lse_h[b, g * G:(g + 1) * G], rl[0]))
     print(f"  {len(units)} units, max-abs {worst:.3e} (tol {w.tol})", flush=True)
     assert worst <= w.tol
+
+    def rows_of(b):
+        n = int(lens_h[b])
+        deq = lambda c, sc: c[b, :, :n].view(torch.float8_e4m3fn).float() * sc[:, None, None]
+        return deq(k, ks), deq(v, vs)
+
+    rows = check_every_unit(q, rows_of, lens_h, out, lse, w.tol)
+    print(f"  all {rows} output rows inside the value hull, lse inside its bounds", flush=True)
     del k, v
     torch.cuda.empty_cache()

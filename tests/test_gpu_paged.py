@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_cases import max_abs, sampled_units, to_dev, to_host
+from tests.gpu_cases import check_every_unit, dense_rows, max_abs, sampled_units, to_dev, to_host
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -143,5 +143,7 @@ def test_paged_workload_full_size(fd, w):
     out_d, lse_d = fd.decode_attn(q, k_dense, v_dense, lens, n_splits=w.n_splits, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out_d) and torch.equal(lse, lse_d)
+    rows = check_every_unit(q, dense_rows(k_dense, v_dense, lens_h), lens_h, out, lse, w.tol)
+    print(f"  all {rows} output rows inside the value hull, lse inside its bounds", flush=True)
     del kp, vp, k_dense, v_dense
     torch.cuda.empty_cache()

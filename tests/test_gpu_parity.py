@@ -82,13 +82,19 @@ def test_boundary_lengths(fd, lens_one):
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16, 32])
-def test_both_partial_kernels(fd, monkeypatch, kernel, G):
-    # FD_PARTIAL_KERNEL forces one of the two partial kernels (bf16, D 128)
-    monkeypatch.setenv("FD_PARTIAL_KERNEL", kernel)
+def test_both_partial_kernels(fd, kernel, G):
+    # the test entry point runs one of the two partial kernels (bf16, D 128)
     Hkv = 2
     case = synth.decode_case(2, G * Hkv, Hkv, 128, 1300, "bf16", seed=300 + G, lens=[1300, 555])
+    q, k, v = (to_dev(case[x], "bf16") for x in ("q", "k", "v"))
+    lens = torch.from_numpy(case["lens"]).to("cuda")
+    ref_out, ref_lse = oracle.attention(case["q"], case["k"], case["v"], case["lens"])
     for ns in (1, 6):
-        check_decode(fd, case, "bf16", n_splits=ns)
+        out, lse = fd.testing_decode_attn(q, k, v, kernel, lens=lens, n_splits=ns, return_lse=True)
+        torch.cuda.synchronize()
+        e_out, e_lse = max_abs(to_host(out), ref_out), max_abs(to_host(lse), ref_lse)
+        print(f"  {kernel} n_splits={ns} max-abs out {e_out:.3e} lse {e_lse:.3e}", flush=True)
+        assert e_out <= TOL["bf16"] and e_lse <= TOL["bf16"]
 
 
 def test_bf16_output_and_explicit_scale(fd):
@@ -215,6 +221,35 @@ def test_bifurcated_small(fd, shape):
     assert e_o <= 1e-2 and e_l <= 1e-2
 
 
+def test_concatenated_cache_matches_oracle(fd):
+    """Split-KV decode attention over the explicitly concatenated cache
+    [context ; own decode rows] -- the non-bifurcated way to the bifurcated
+    result -- at a reduced bifurcated-GQA shape (16 samples, 4096 context
+    rows, decode rows uniform in [1, 512], 32 query / 8 KV heads), element by
+    element against the oracle, both as plain attention over the
+    concatenated rows and as bifurcated attention ([BA] "Tiivistelmä")."""
+    S, Hq, Hkv, D, Lc, Ld = 16, 32, 8, 128, 4096, 512
+    case = synth.bifurcated_case(S, Hq, Hkv, D, Lc, Ld, "bf16", seed=8100, dec_lens=(1, 512))
+    kcat = np.concatenate([np.broadcast_to(case["k_ctx"][None], (S, Hkv, Lc, D)), case["k_dec"]], axis=2)
+    vcat = np.concatenate([np.broadcast_to(case["v_ctx"][None], (S, Hkv, Lc, D)), case["v_dec"]], axis=2)
+    lens = (case["dec_lens"] + Lc).astype(np.int32)
+    q = to_dev(case["q"], "bf16")
+    out, lse = fd.decode_attn(q, to_dev(kcat, "bf16"), to_dev(vcat, "bf16"), torch.from_numpy(lens).cuda(),
+                              return_lse=True)
+    t = {k: to_dev(case[k], "bf16") for k in ("k_ctx", "v_ctx", "k_dec", "v_dec")}
+    bif, bif_lse = fd.bifurcated_attn(q, t["k_ctx"], t["v_ctx"], t["k_dec"], t["v_dec"],
+                                      torch.from_numpy(case["dec_lens"]).cuda(), return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(case["q"], kcat, vcat, lens)
+    ref_bo, ref_bl = oracle.bifurcated_attention(case["q"], case["k_ctx"], case["v_ctx"], case["k_dec"],
+                                                 case["v_dec"], case["dec_lens"])
+    assert max_abs(ref_o, ref_bo) <= 1e-12 and max_abs(ref_l, ref_bl) <= 1e-12
+    e = [max_abs(to_host(out), ref_o), max_abs(to_host(lse), ref_l),
+         max_abs(to_host(bif), ref_o), max_abs(to_host(bif_lse), ref_l)]
+    print(f"  concatenated out {e[0]:.3e} lse {e[1]:.3e}; bifurcated out {e[2]:.3e} lse {e[3]:.3e}", flush=True)
+    assert max(e) <= 1e-2
+
+
 def test_bifurcated_equals_decode_on_concatenated_cache(fd):
     S, Hq, Hkv, D, Lc, Ld = 4, 16, 2, 128, 1500, 80
     case = synth.bifurcated_case(S, Hq, Hkv, D, Lc, Ld, "bf16", seed=31, dec_lens=[80, 3, 0, 41])
@@ -226,3 +261,35 @@ def test_bifurcated_equals_decode_on_concatenated_cache(fd):
     cat = fd.decode_attn(t["q"], kc, vc, (dlen + Lc).to(torch.int32))
     torch.cuda.synchronize()
     assert max_abs(to_host(bif), to_host(cat)) <= 2e-3
+
+
+# ------------------------------------------------------- large |V| values
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Lmax, lens
+    (2, 16, 2, 1500, [1500, 3]),      # matrix-core kernel, G = 8
+    (1, 32, 1, 900, [900]),           # matrix-core kernel, MQA: 32-row units
+    (2, 8, 8, 700, [700, 40]),        # vector-ALU kernel (MHA)
+    (2, 12, 4, 600, [600, 17]),       # vector-ALU kernel, G = 3
+], ids=lambda s: f"B{s[0]}_hq{s[1]}_hkv{s[2]}")
+@pytest.mark.parametrize("v_scale", [8.0, 64.0])
+def test_large_values_hold_the_flat_bound(fd, shape, v_scale):
+    """V entries of N(0, v_scale^2) (|v| up to about 4.5 v_scale, bf16) and
+    K scaled by 3 (sharp softmax, a few rows of similar weight): the
+    split-KV kernels keep max-abs 1e-2 on fp32 outputs, independent of the
+    spread of V."""
+    B, Hq, Hkv, L, lens = shape
+    case = synth.decode_case(B, Hq, Hkv, 128, L, "bf16", seed=610 + Hq, lens=lens)
+    case["v"] = synth.round_to_bf16(case["v"] * np.float32(v_scale))
+    case["k"] = synth.round_to_bf16(case["k"] * np.float32(3.0))
+    for ns in (0, 1, 5):
+        check_decode(fd, case, "bf16", n_splits=ns, out_dtype=torch.float32)
+    # the other partial kernel on the same shape, where it supports it
+    q, k, v = (to_dev(case[x], "bf16") for x in ("q", "k", "v"))
+    lens_d = torch.from_numpy(case["lens"]).to("cuda")
+    ref_out, ref_lse = oracle.attention(case["q"], case["k"], case["v"], case["lens"])
+    for kernel in ("valu", "mfma"):
+        out, lse = fd.testing_decode_attn(q, k, v, kernel, lens=lens_d, n_splits=3, out_dtype=torch.float32,
+                                          return_lse=True)
+        torch.cuda.synchronize()
+        assert max_abs(to_host(out), ref_out) <= TOL["bf16"] and max_abs(to_host(lse), ref_lse) <= TOL["bf16"]

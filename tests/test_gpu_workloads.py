@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_cases import max_abs, oracle_decode_rows, sampled_units, to_host
+from tests.gpu_cases import check_every_unit, dense_rows, max_abs, oracle_decode_rows, sampled_units, to_host
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -51,6 +51,9 @@ def test_decode_workload_full_size(fd, w):
         worst = max(worst, max_abs(out_h[b, rows], ro), max_abs(lse_h[b, rows], rl))
     print(f"  {len(units)} units, max-abs {worst:.3e} (tol {w.tol})", flush=True)
     assert worst <= w.tol
+    lens_h = lens.cpu().numpy()
+    rows = check_every_unit(q, dense_rows(k, v, lens_h), lens_h, out, lse, w.tol)
+    print(f"  all {rows} output rows inside the value hull, lse inside its bounds", flush=True)
     del q, k, v
     torch.cuda.empty_cache()
 
@@ -95,3 +98,49 @@ def test_bifurcated_workload_full_size(fd, w):
         worst = max(worst, max_abs(out_h[s:s + 1], ro), max_abs(lse_h[s:s + 1], rl))
     print(f"  samples {samples}, max-abs {worst:.3e} (tol {w.tol})", flush=True)
     assert worst <= w.tol
+
+    # every sample: its rows are [context ; own valid decode rows]
+    def rows_of(s):
+        n = int(dl_h[s])
+        return (torch.cat([t["k_ctx"], t["k_dec"][s, :, :n]], dim=1).float(),
+                torch.cat([t["v_ctx"], t["v_dec"][s, :, :n]], dim=1).float())
+
+    n_rows = check_every_unit(t["q"], rows_of, dl_h + w.ctx_len, out, lse, w.tol)
+    print(f"  all {n_rows} output rows inside the value hull, lse inside its bounds", flush=True)
+
+
+@pytest.mark.parametrize("w", configs.ALL_BIFURCATED, ids=lambda w: w.name)
+def test_concatenated_cache_full_size(fd, w):
+    """The non-bifurcated way to the same result: split-KV decode attention
+    (planner split count, as the bench times it) over the explicitly
+    concatenated cache [context ; own decode rows] per sample, at full size.
+    Sampled samples (first, last, shortest and longest decode part) against
+    the oracle's plain attention over those rows ([BA] "Tiivistelmä": both
+    ways compute the same attention)."""
+    print(f"  workload {w.name} (concatenated cache)", flush=True)
+    t, dl = make_bifurcated(w)
+    S, Hkv, Lc, Ld, D = w.samples, w.kv_heads, w.ctx_len, w.dec_max, w.head_dim
+    kc = torch.empty((S, Hkv, Lc + Ld, D), dtype=t["k_ctx"].dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[:, :, :Lc] = t["k_ctx"].unsqueeze(0)
+    vc[:, :, :Lc] = t["v_ctx"].unsqueeze(0)
+    kc[:, :, Lc:] = t["k_dec"]
+    vc[:, :, Lc:] = t["v_dec"]
+    lens = (dl + Lc).to(torch.int32)
+    out, lse = fd.decode_attn(t["q"], kc, vc, lens, return_lse=True)
+    torch.cuda.synchronize()
+    out_h, lse_h = to_host(out), to_host(lse)
+    assert np.all(np.isfinite(out_h))
+    dl_h = dl.cpu().numpy()
+    samples = sorted({0, S - 1, int(np.argmin(dl_h)), int(np.argmax(dl_h))})
+    units = [(s, g) for s in samples for g in sorted({0, Hkv - 1})]
+    ref = oracle_decode_rows(t["q"], kc, vc, lens, units)
+    G = w.q_heads // Hkv
+    worst = 0.0
+    for (s, g), (ro, rl) in ref.items():
+        rows = slice(g * G, (g + 1) * G)
+        worst = max(worst, max_abs(out_h[s, rows], ro), max_abs(lse_h[s, rows], rl))
+    print(f"  {len(units)} units, max-abs {worst:.3e} (tol {w.tol})", flush=True)
+    assert worst <= w.tol
+    del kc, vc
+    torch.cuda.empty_cache()

@@ -26,7 +26,7 @@ def _mutant(**overrides):
         split_partials=oa.split_partials, lse_combine=oa.lse_combine,
         default_scale=oa.default_scale, paged_attention=oa.paged_attention,
         fp8_e4m3_value=oa.fp8_e4m3_value, attention_fp8kv=oa.attention_fp8kv,
-        prefill_attention=oa.prefill_attention)
+        prefill_attention=oa.prefill_attention, bifurcated_paged_attention=oa.bifurcated_paged_attention)
     for name, fn in overrides.items():
         setattr(ns, name, fn)
     return ns
@@ -134,6 +134,31 @@ def _paged_gather(mapping):
     return paged
 
 
+def _bif_paged_gather(mapping, keep_context=True):
+    """bifurcated_paged_attention with the decode row -> (page, slot) mapping
+    replaced (or the context left out)."""
+    def bif(q, k_ctx, v_ctx, k_pages, v_pages, block_table, dec_lens, scale=None):
+        k_pages, v_pages = np.asarray(k_pages, np.float64), np.asarray(v_pages, np.float64)
+        table = np.asarray(block_table)
+        S, P, D = table.shape[0], k_pages.shape[2], k_pages.shape[3]
+        Ld = table.shape[1] * P
+        kd = np.full((S, k_pages.shape[1], Ld, D), np.nan)
+        vd = np.full_like(kd, np.nan)
+        for s_ in range(S):
+            for t in range(int(dec_lens[s_])):
+                page, slot, _ = mapping(table, s_, t, P)
+                kd[s_, :, t] = k_pages[page, :, slot]
+                vd[s_, :, t] = v_pages[page, :, slot]
+        if not keep_context:
+            k_ctx, v_ctx = np.asarray(k_ctx)[:, :1] * 0.0, np.asarray(v_ctx)[:, :1] * 0.0
+        return oa.bifurcated_attention(q, k_ctx, v_ctx, kd, vd, dec_lens, scale)
+    return bif
+
+
+def _map_identity(table, b, t, P):
+    return table[b, t // P], t % P, False
+
+
 def _map_page_slot_swapped(table, b, t, P):
     return table[b, t % P], t // P, False
 
@@ -214,6 +239,12 @@ MUTANTS = {
     "paged_table_transposed": lambda: _mutant(paged_attention=_paged_gather(_map_table_transposed)),
     "paged_head_axis_swapped": lambda: _mutant(paged_attention=_paged_gather(_map_head_axis_swapped)),
     "paged_wrong_slot_in_tail": lambda: _mutant(paged_attention=_paged_gather(_map_whole_last_page)),
+    "bifurcated_paged_page_slot_swapped": lambda: _mutant(
+        bifurcated_paged_attention=_bif_paged_gather(_map_page_slot_swapped)),
+    "bifurcated_paged_table_transposed": lambda: _mutant(
+        bifurcated_paged_attention=_bif_paged_gather(_map_table_transposed)),
+    "bifurcated_paged_context_dropped": lambda: _mutant(
+        bifurcated_paged_attention=_bif_paged_gather(_map_identity, keep_context=False)),
     "fp8_exponent_bias_8": lambda: _mutant(fp8_e4m3_value=_fp8_bias8, attention_fp8kv=_fp8_with(_fp8_bias8)),
     "fp8_subnormals_as_normals": lambda: _mutant(fp8_e4m3_value=_fp8_no_subnormals,
                                                  attention_fp8kv=_fp8_with(_fp8_no_subnormals)),
