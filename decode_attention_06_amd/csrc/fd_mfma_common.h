@@ -101,28 +101,33 @@ __device__ __forceinline__ void pv_packed(const u32x4_t (&vr)[8], const bf16x8_t
 // (acc / l) and lse (m + log2 l) do not depend on the reference chosen.
 constexpr float MF_RESCALE_SLACK = 8.0f;
 
+// The k-steps run outermost, so consecutive products go to different
+// accumulators (2 NRB independent chains) instead of one chain of four
+// dependent products at a time.
 template <int NRB>
 __device__ __forceinline__ void tile_scores(const u32x4_t (&kr)[2][4], const bf16x8_t (&qb)[NRB][4],
                                             f32x4_t (&sc)[NRB][2]) {
 #pragma unroll
     for (int r = 0; r < NRB; ++r)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sc[r][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int blk = 0; blk < 2; ++blk) sc[r][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
                 sc[r][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[blk][s]), qb[r][s], sc[r][blk], 0, 0, 0);
-        }
 }
 
 // tmask (wave-uniform): no token below it is masked for any row of the
 // wave; lim[r]: the lane's row of block r sees tokens below lim[r] only.
 //
-// SPLIT: each fp32 weight w leaves as two bf16 values, pb = bf16(w) and
-// pl = bf16(w - pb) (w - pb is exact in fp32).  pb + pl is within
-// 2^-17 |w| of w, so the weights the products see are fp32-accurate and the
-// output error no longer grows with the spread of V (one bf16 weight is off
-// by up to 2^-9 |w|: about 2^-9 |v1 - v2| at the output).  The running sum
+// SPLIT: each fp32 weight w leaves as two bf16 values, pb = w cut to its
+// top 16 bits and pl = bf16(w - pb) (w - pb is exact in fp32).  pb + pl is
+// within 2^-17 |w| of w, so the weights the products see are fp32-accurate
+// and the output error no longer grows with the spread of V (one bf16 weight
+// is off by up to 2^-9 |w|: about 2^-9 |v1 - v2| at the output).  The running sum
 // then takes the fp32 weights themselves: `lsum` (a float per row) holds the
 // sum over this lane's tokens only, and the caller adds the four lane
 // groups of a row at the end.  Without SPLIT, `lsum` is an f32x4 whose
