@@ -228,18 +228,16 @@ hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, 
     const int64_t n_dec = (dec_units + XCDS - 1) / XCDS * XCDS * d.row_blocks;
     const int64_t wgs = ((n_ctx + XCDS - 1) / XCDS + (n_dec + XCDS - 1) / XCDS) * XCDS;
     if (n_ctx >= (1 << 30) || n_dec >= (1 << 30)) return hipErrorInvalidValue;
-    // Groups of at most 8 query heads: the decode role packs its weight
-    // remainders into the 16-row block's padding columns.
-    const bool pack = d.Hq / d.Hkv <= 8;
+    // Groups of at most 8 query heads on a dense decode cache: the decode
+    // role packs its weight remainders into the 16-row block's padding
+    // columns (the paged form keeps two products per block: packing there
+    // needs more registers than two workgroups per CU leave).
+    const bool pack = d.Hq / d.Hkv <= 8 && !d.block_table;
 #define FD_BIF(PG, PK) hipLaunchKernelGGL((bifurcated_kernel<PG, PK>), dim3((unsigned)wgs), dim3(256), 0, stream, c, d, \
                                           (int)n_ctx, (int)n_dec)
-    if (d.block_table) {
-        if (pack) FD_BIF(true, true);
-        else FD_BIF(true, false);
-    } else {
-        if (pack) FD_BIF(false, true);
-        else FD_BIF(false, false);
-    }
+    if (d.block_table) FD_BIF(true, false);
+    else if (pack) FD_BIF(false, true);
+    else FD_BIF(false, false);
 #undef FD_BIF
     return hipGetLastError();
 }

@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fd_device.h"
 
 namespace fd {
@@ -138,7 +140,10 @@ __device__ __forceinline__ void tile_scores(const u32x4_t (&kr)[2][4], const bf1
 // bottleneck (many query rows per KV tile) keep one bf16 weight.
 //
 // PACK (see compute_tile): accumulator columns 8..15 hold the remainder
-// shares of rows 0..7, so a rescale applies row i's factor to column i + 8.
+// shares of rows 0..7, so a rescale applies row i's factor to column i + 8;
+// the running sum is then an f32x4 formed like the accumulators, by a
+// product of a block of ones with the packed weights (compute_tile), and
+// column i + 8 of it holds row i's remainder sum.
 template <int NRB, bool SPLIT, typename SumT, bool PACK = false>
 __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb, int tmask, const int (&lim)[NRB],
                                              int g, float sl2, float (&m)[NRB], SumT (&lsum)[NRB],
@@ -185,7 +190,6 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
             x = fmaxf(x, __shfl_xor(x, 32));
             const float mn = fmaxf(m[r], x * sl2);
             const float alpha = fast_exp2(m[r] - ((mn == -INFINITY) ? 0.f : mn));
-            lsum[r] *= alpha;
             float acc_alpha = alpha;
             if constexpr (PACK) {
                 // row_shr:8 into banks 2 and 3: lane i + 8 of a 16-lane row
@@ -193,6 +197,8 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
                 acc_alpha = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(alpha), __float_as_int(alpha),
                                                                         0x118, 0xF, 0xC, false));
             }
+            // PACK: the sums' columns 8..15 are rows 0..7's remainder sums too
+            lsum[r] *= PACK ? acc_alpha : alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[r][e] *= acc_alpha;
             m[r] = mn;
@@ -218,7 +224,7 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
                 r2.x = (__bf16)(w0 - __uint_as_float(u0 & 0xffff0000u));
                 r2.y = (__bf16)(w1 - __uint_as_float(u1 & 0xffff0000u));
                 lw[j >> 1] = __builtin_bit_cast(uint32_t, r2);
-                lsum[r] += w0 + w1;
+                if constexpr (!PACK) lsum[r] += w0 + w1;
             }
             pb[r] = __builtin_bit_cast(bf16x8_t, hw);
             pl[r] = __builtin_bit_cast(bf16x8_t, lw);
@@ -246,10 +252,13 @@ __device__ __forceinline__ void tile_softmax(const f32x4_t (&sc)[NRB][2], int tb
 // product per output block takes both parts; column i + 8 of the result
 // then holds row i's remainder share, which pack_fold() adds back once per
 // piece.
+template <bool PACK>
+using SplitSum = typename std::conditional<PACK, f32x4_t, float>::type;
+
 template <int NRB, bool PACK = false>
 __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vr)[8],
                                              const bf16x8_t (&qb)[NRB][4], int tb, int t1, int g, float sl2,
-                                             float (&m)[NRB], float (&lsum)[NRB], f32x4_t (&acc)[NRB][8]) {
+                                             float (&m)[NRB], SplitSum<PACK> (&lsum)[NRB], f32x4_t (&acc)[NRB][8]) {
     static_assert(!PACK || NRB == 1, "packing needs one block with spare columns");
     f32x4_t sc[NRB][2];
     tile_scores<NRB>(kr, qb, sc);
@@ -257,7 +266,7 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
     int lim[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) lim[r] = t1;
-    tile_softmax<NRB, true, float, PACK>(sc, tb, t1, lim, g, sl2, m, lsum, acc, pb, pl);
+    tile_softmax<NRB, true, SplitSum<PACK>, PACK>(sc, tb, t1, lim, g, sl2, m, lsum, acc, pb, pl);
     if constexpr (PACK) {
         const u32x4_t hi = __builtin_bit_cast(u32x4_t, pb[0]);
         const u32x4_t lo = __builtin_bit_cast(u32x4_t, pl[0]);
@@ -269,6 +278,10 @@ __device__ __forceinline__ void compute_tile(const u32x4_t (&kr)[2][4], const u3
             pk[k] = (uint32_t)__builtin_amdgcn_update_dpp((int)hi[k], (int)lo[k], 0x118, 0xF, 0xC, false);
         }
         const bf16x8_t pp = __builtin_bit_cast(bf16x8_t, pk);
+        if constexpr (PACK) {
+            const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+            lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pp, lsum[0], 0, 0, 0);
+        }
         pv_packed<0>(vr, pp, acc[0]);
         pv_packed<1>(vr, pp, acc[0]);
         pv_packed<2>(vr, pp, acc[0]);

@@ -94,14 +94,14 @@ __device__ __forceinline__ void load_rows(const uint8_t* kpool, const uint8_t* v
 // Computes one loaded tile (see compute_tile).
 template <int NRB, bool PACK>
 __device__ __forceinline__ void compute_loaded(const Bf16Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
-                                               int g, float sl2, float (&m)[NRB], float (&lsum)[NRB],
+                                               int g, float sl2, float (&m)[NRB], SplitSum<PACK> (&lsum)[NRB],
                                                f32x4_t (&acc)[NRB][8]) {
     compute_tile<NRB, PACK>(r.k, r.v, qb, tb, t1, g, sl2, m, lsum, acc);
 }
 
 template <int NRB, bool PACK>
 __device__ __forceinline__ void compute_loaded(const Fp8Tile& r, const bf16x8_t (&qb)[NRB][4], int tb, int t1,
-                                               int g, float sl2, float (&m)[NRB], float (&lsum)[NRB],
+                                               int g, float sl2, float (&m)[NRB], SplitSum<PACK> (&lsum)[NRB],
                                                f32x4_t (&acc)[NRB][8]) {
     u32x4_t kr[2][4], vr[8];
 #pragma unroll
@@ -230,11 +230,15 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     const float vsc = p.v_scale ? p.v_scale[kvh] : 1.f;
 
     f32x4_t acc[NRB][8];
-    float m[NRB], lsum[NRB];   // lsum: this lane's share of its row's running sum
+    // lsum: the running sum; a float per row holding this lane's share
+    // (summed over the lane groups at the end), or with PACK an f32x4 whose
+    // components hold the whole row sum (columns 8..15: the remainders')
+    float m[NRB];
+    SplitSum<PACK> lsum[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         m[r] = -INFINITY;
-        lsum[r] = 0.f;
+        lsum[r] = SplitSum<PACK>{};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -298,18 +302,23 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
     // Every lane computes its rows' merged max M and sum L from the waves'
     // (m, l) and scales its own accumulators by exp2(m - M) / L in
     // registers; what is left per output element is a plain sum over waves.
+    float lrow[NRB];   // each lane: its row's complete running sum
+    if constexpr (PACK) {
+        pack_fold(acc);
+        lrow[0] = lsum[0][0] + dpp<0x108>(lsum[0][0]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        lsum[r] += __shfl_xor(lsum[r], 16);
-        lsum[r] += __shfl_xor(lsum[r], 32);
+        for (int r = 0; r < NRB; ++r) {
+            lrow[r] = lsum[r] + __shfl_xor(lsum[r], 16);
+            lrow[r] += __shfl_xor(lrow[r], 32);
+        }
     }
-    if constexpr (PACK) pack_fold(acc);
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         const int row = r * 16 + i;
         if (g == 0 && row < nr) {
             s_m[wave][row] = m[r];
-            s_l[wave][row] = lsum[r];
+            s_l[wave][row] = lrow[r];
         }
     }
     __syncthreads();

@@ -1,6 +1,7 @@
 """fd_bifurcated_attn_paged: each sample's decode rows in a shuffled page
-pool, against the fp64 oracle (bifurcated_paged_attention) and bit for bit
-against fd_bifurcated_attn on the gathered decode cache.
+pool, against the fp64 oracle (bifurcated_paged_attention) and against
+fd_bifurcated_attn on the gathered decode cache: bit for bit where both
+decode roles use the same tile layout, else to 1e-5.
 
 Page 0 and the rows past dec_lens[s] in a used page are NaN, and unused
 table entries are -1, so any read outside the valid rows poisons the
@@ -42,7 +43,15 @@ def test_bifurcated_paged_matches_oracle_and_dense(fd, shape):
     dense, dense_lse = fd.bifurcated_attn(t["q"], t["k_ctx"], t["v_ctx"], kd, vd, dlen, return_lse=True)
     torch.cuda.synchronize()
     assert np.all(np.isfinite(to_host(got)))
-    assert np.array_equal(to_host(got), to_host(dense)) and np.array_equal(to_host(got_lse), to_host(dense_lse))
+    if dt == "bf16" and Hq // Hkv <= 8:
+        # the dense decode role packs two heads' weights per matrix-core
+        # tile and keeps its running sums there; the paged one does not, so
+        # the two round the row sums in a different order
+        assert max_abs(to_host(got), to_host(dense)) <= 1e-5
+        assert max_abs(to_host(got_lse), to_host(dense_lse)) <= 1e-5
+    else:
+        assert np.array_equal(to_host(got), to_host(dense))
+        assert np.array_equal(to_host(got_lse), to_host(dense_lse))
     ref_o, ref_l = oracle.bifurcated_paged_attention(case["q"], case["k_ctx"], case["v_ctx"], kp, vp, table,
                                                      case["dec_lens"])
     tol = 1e-5 if dt == "fp32" else 1e-2
