@@ -149,7 +149,45 @@ def timed_eager(fn, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def time_decode(w, steps, warmup, force_splits=0):
+ISOLATION_US = 300.0      # spin ahead of each isolated step: covers the host's launch of the step
+
+
+def step_percentiles(fn, copies, samples):
+    """Each step on its own: launched eagerly behind a spin kernel of about
+    ISOLATION_US (calibrated here), so the host has queued the step's
+    kernels before the GPU reaches them, and bracketed by two HIP events on
+    its stream.  Copies rotate as in the timed loop, so every step reads
+    cold inputs.  Returns the p10, median and p90 of the per-step times in
+    ms, and the number of samples."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cal = 100000
+    torch.cuda._sleep(cal)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    torch.cuda._sleep(cal)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycles = max(cal, int(cal * ISOLATION_US * 1e-3 / max(e0.elapsed_time(e1), 1e-6)))
+    for j in range(min(copies, 2)):
+        fn(j)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for i, (a, b) in enumerate(ev):
+        torch.cuda._sleep(cycles)
+        a.record(stream)
+        fn(i % copies)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    p10, p50, p90 = np.percentile(t, [10, 50, 90])
+    return {"p10_ms": float(p10), "median_ms": float(p50), "p90_ms": float(p90), "samples": int(samples)}
+
+
+def time_decode(w, steps, warmup, force_splits=0, probe=True, percentiles=True, want_host=True):
     import torch
 
     import decode_attention_06_amd as fd
@@ -194,24 +232,33 @@ def time_decode(w, steps, warmup, force_splits=0):
     eager_ms = timed_eager(step, steps)
     step_ms = timed_graph(step, steps)
     kern_ms = timed_graph(partial_only, steps)
+    pct = step_percentiles(step, copies, max(steps, 2 * copies)) if percentiles else None
 
-    # Plain read of the same number of bytes, rotated the same way.
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    # Plain read of the same number of bytes in ONE launch per step, over
+    # buffers rotated the same way: the single-launch read ceiling.
+    probe_gbs = None
+    if probe:
+        probe_bytes = 2 * sets[0][1].numel() * sets[0][1].element_size()
+        bufs = [torch.empty(probe_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        for b_ in bufs:
+            b_.fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def probe(j):
-        q, k, v = sets[j % copies]
-        fd.read_probe(k, sink)
-        fd.read_probe(v, sink)
+        def probe_step(j):
+            fd.read_probe(bufs[j % copies], sink)
 
-    probe_ms = timed_graph(probe, steps)
-    probe_bytes = 2 * sets[0][1].numel() * sets[0][1].element_size()
+        probe_ms = timed_graph(probe_step, steps)
+        probe_gbs = probe_bytes / (probe_ms * 1e-3) / 1e9
+        del bufs
 
     info = {
         "n_splits": ns, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": kern_ms,
-        "eager_step_ms": eager_ms, "probe_gbs": probe_bytes / (probe_ms * 1e-3) / 1e9,
+        "eager_step_ms": eager_ms, "probe_gbs": probe_gbs, "percentiles": pct,
         "kernel": "partial_mfma_kernel" if mfma else "partial_valu_kernel",
         "flops": 4 * int(lens.sum().item()) * w.q_heads * w.head_dim,
     }
+    if not want_host:
+        return info, None
     host = [t.detach().float().cpu().numpy() for t in sets[0]]
     return info, (host, lens.cpu().numpy())
 
@@ -351,7 +398,7 @@ def time_concatenated(w, sets, dl, steps):
     return ms, ns
 
 
-def time_bifurcated(w, steps, warmup, compare_concat=False):
+def time_bifurcated(w, steps, warmup, compare_concat=False, percentiles=True):
     import torch
 
     import decode_attention_06_amd as fd
@@ -378,11 +425,69 @@ def time_bifurcated(w, steps, warmup, compare_concat=False):
     torch.cuda.synchronize()
     eager_ms = timed_eager(step, steps)
     step_ms = timed_graph(step, steps)
+    pct = step_percentiles(step, copies, max(steps, 2 * copies)) if percentiles else None
     info = {"n_splits": None, "copies": copies, "kv_bytes": kv_bytes, "step_ms": step_ms, "kernel_ms": step_ms,
-            "eager_step_ms": eager_ms, "probe_gbs": None, "kernel": "bifurcated (whole call)", "flops": flops}
+            "eager_step_ms": eager_ms, "probe_gbs": None, "kernel": "bifurcated (whole call)", "flops": flops,
+            "percentiles": pct}
     if compare_concat:
         info["concat_ms"], info["concat_splits"] = time_concatenated(w, sets, dl, max(5, steps // 4))
     return info, None
+
+
+# ------------------------------------------------ every other workload
+
+# The other workloads of the method, measured in the same run as the
+# headline: the tiny fp32 case, MHA over 64K tokens at batch 1 and 16, and
+# the two bifurcated workloads with split-KV over the concatenated cache
+# (the non-bifurcated way to the same result) beside them.
+EXTRA_DECODE = (configs.TINY,) + tuple(w for w in configs.MHA_SWEEP if w.max_len == 65536)
+EXTRA_BIFURCATED = configs.ALL_BIFURCATED
+
+
+def _pct_us(info):
+    p = info.get("percentiles")
+    if not p:
+        return {}
+    return {"p10_us": round(p["p10_ms"] * 1e3, 3), "median_us": round(p["median_ms"] * 1e3, 3),
+            "p90_us": round(p["p90_ms"] * 1e3, 3), "isolated_samples": p["samples"]}
+
+
+def run_extras(steps, warmup):
+    """One record per workload: mean µs per step over a graph replay of
+    `steps` steps, the p10 / median / p90 of steps timed one by one, the KV
+    read rate as a fraction of 8 TB/s, and the kernel-level figures."""
+    import torch
+
+    recs = []
+    for w in EXTRA_DECODE:
+        log(f"[bench] extra workload {w.name}")
+        info, _ = time_decode(w, steps, warmup, probe=False, want_host=False)
+        step_s, kern_s = info["step_ms"] * 1e-3, info["kernel_ms"] * 1e-3
+        rec = {"workload": w.name, "us_per_step": round(info["step_ms"] * 1e3, 3), **_pct_us(info),
+               "kv_bytes": info["kv_bytes"], "tb_per_s": round(info["kv_bytes"] / step_s / 1e12, 4),
+               "hbm_frac": round(info["kv_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+               "kernel": info["kernel"], "kernel_us": round(info["kernel_ms"] * 1e3, 3),
+               "kernel_hbm_frac": round(info["kv_bytes"] / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+               "n_splits": info["n_splits"], "dtype": w.dtype}
+        recs.append(rec)
+        log(f"[bench]   {rec}")
+        torch.cuda.empty_cache()
+    for w in EXTRA_BIFURCATED:
+        log(f"[bench] extra workload {w.name}")
+        info, _ = time_bifurcated(w, steps, warmup, compare_concat=True)
+        step_s = info["step_ms"] * 1e-3
+        rec = {"workload": w.name, "us_per_step": round(info["step_ms"] * 1e3, 3), **_pct_us(info),
+               "kv_bytes": info["kv_bytes"], "tb_per_s": round(info["kv_bytes"] / step_s / 1e12, 4),
+               "hbm_frac": round(info["kv_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+               "flops": info["flops"], "tflops": round(info["flops"] / step_s / 1e12, 2),
+               "mfma_frac": round(info["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "concatenated_us_per_step": round(info["concat_ms"] * 1e3, 3),
+               "concatenated_n_splits": info["concat_splits"],
+               "speedup_vs_concatenated": round(info["concat_ms"] / info["step_ms"], 3), "dtype": w.dtype}
+        recs.append(rec)
+        log(f"[bench]   {rec}")
+        torch.cuda.empty_cache()
+    return recs
 
 
 # --------------------------------------------------------- CPU baseline
@@ -450,6 +555,8 @@ def main():
     ap.add_argument("--compare-concat", action="store_true",
                     help="bifurcated workloads: also time split-KV decode over the concatenated cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads (the 'extra' object)")
+    ap.add_argument("--extra-steps", type=int, default=20, help="timed steps per extra workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -557,6 +664,10 @@ def main():
                             "kernel_us": round(info["kernel_ms"] * 1e3, 3), "flops": info["flops"]}
     if "kernel_timing" in info:
         line["roofline"]["kernel_timing"] = info["kernel_timing"]
+    pct = _pct_us(info)
+    if pct:
+        line["step_percentiles"] = dict(pct, timing="each step alone, launched behind a spin kernel that covers "
+                                                    "the host's launch, between two HIP events")
     if bif:
         line["roofline"]["mfma_tflops"] = round(info["flops"] / step_s / 1e12, 2)
         line["roofline"]["mfma_frac"] = round(info["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
@@ -565,6 +676,12 @@ def main():
             line["speedup_vs_concatenated"] = round(info["concat_ms"] / info["step_ms"], 3)
             log(f"[bench] same result by split-KV over the concatenated cache: {info['concat_ms'] * 1e3:.2f} us "
                 f"({info['concat_splits']} pieces); bifurcated speedup {info['concat_ms'] / info['step_ms']:.2f}x")
+    if not args.no_extra and w.name == DEFAULT_WORKLOAD:
+        del host
+        torch.cuda.empty_cache()
+        line["extra"] = {"timing": "as the headline: mean over a graph replay of the steps; p10 / median / p90 "
+                                   "of steps timed one by one behind a spin kernel", "steps": args.extra_steps,
+                         "workloads": run_extras(args.extra_steps, min(args.warmup, 5))}
     print(json.dumps(line), flush=True)
     return 0
 
