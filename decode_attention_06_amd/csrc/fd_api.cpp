@@ -134,13 +134,17 @@ constexpr int64_t kMinContextPiece = 256;   // shortest context piece planned
 
 // Pieces for the context and for the decode part of a bifurcated call.  The
 // matrix-core context kernel (bf16, D 128) works on tiles of query rows and
-// shares its launch with the decode units (one piece each).  Of the two
-// workgroup slots per CU, the context units take what the decode units leave
-// but at least three quarters: the decode units then stream their rows from
-// HBM beside the context units from the start, and the context pieces stay
-// long enough that their partials (one per row and piece, written and read
-// back by the combine) cost little.  Otherwise the context goes through the
-// split-KV kernel like a batch of S sequences.
+// shares its launch with the decode units (one piece each).  When the
+// decode workgroups fit in one of the two workgroup slots per CU, the
+// context units take one slot on every CU: a context workgroup alone on a
+// CU runs its tiles about 13% faster than two side by side, and the
+// HBM-bound decode workgroups share CUs with them.  Otherwise the context
+// units take what the decode units leave but at least three quarters of the
+// slots: the decode units then stream their rows from HBM beside the
+// context units from the start, and the context pieces stay long enough
+// that their partials (one per row and piece, written and read back by the
+// combine) cost little.  Without the matrix-core context kernel the context
+// goes through the split-KV kernel like a batch of S sequences.
 struct BifPlan {
     bool mfma_ctx;
     int32_t row_tiles;
@@ -156,7 +160,8 @@ BifPlan plan_bifurcated(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t L
         const int64_t units = int64_t(Hkv) * b.row_tiles;
         const int64_t slots = int64_t(n_cu) * kWgPerCu;
         const int64_t dec_units = int64_t(S) * Hkv * ((Hq / Hkv + 15) / 16);
-        const int64_t ctx_wgs = std::max<int64_t>(slots * 3 / 4, slots - dec_units);
+        const int64_t ctx_wgs =
+            dec_units <= n_cu ? int64_t(n_cu) : std::max<int64_t>(slots * 3 / 4, slots - dec_units);
         int64_t pc = (ctx_wgs + units - 1) / units;
         pc = std::min<int64_t>(pc, std::max<int64_t>(1, Lc / kMinContextPiece));
         b.pc = int32_t(std::max<int64_t>(1, std::min<int64_t>(pc, FD_MAX_SPLITS)));

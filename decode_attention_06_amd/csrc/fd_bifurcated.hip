@@ -168,40 +168,29 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
 // units (above) and the decode part's split-KV units (16-row matrix-core
 // blocks, one piece per unit; dense or paged decode cache).  Workgroup ids
 // come in blocks of eight (consecutive ids go to the eight XCDs in turn).
-// When the decode units are few, blocks alternate between the roles in
-// proportion to their counts, so both kinds run side by side from the start
-// -- the decode part streams its own KV from HBM while the context part
-// keeps the matrix cores busy; when they are many, the context blocks come
-// first.  Either way a context unit's row tiles share one XCD, and so do
-// the row blocks of one decode unit (sample, KV head), which also start
-// together: the second reads the decode rows the first brings into that
-// XCD's L2 instead of fetching them again.
+// The context blocks come first, the decode blocks after them: with at most
+// one context workgroup per CU planned, every decode workgroup that fits
+// starts at once beside one, streaming its own KV from HBM while the context
+// part keeps the matrix cores busy; with more, the long context units all
+// start first and the short decode units fill the CUs after them.  A
+// context unit's row tiles share one XCD, and so do the row blocks of one
+// decode unit (sample, KV head), which also start together: the second
+// reads the decode rows the first brings into that XCD's L2 instead of
+// fetching them again.
 template <bool PAGED, bool PACK>
 __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextParams c, const PartialParams d,
                                                             int n_ctx, int n_dec) {
     __shared__ __attribute__((aligned(16))) char lds[CTX_LDS_BYTES];
     static_assert(sizeof(PartialLds<1, 4>) <= CTX_LDS_BYTES, "decode role LDS");
     const int blk = blockIdx.x / XCDS, lane8 = blockIdx.x % XCDS;
-    const int nb_ctx = (n_ctx + XCDS - 1) / XCDS, nb_dec = (n_dec + XCDS - 1) / XCDS;
-    const int nb = nb_ctx + nb_dec;
-    int ctx_before, ctx_after;
-    if (2 * n_dec <= n_ctx) {
-        // Few decode units: spread them among the context units.
-        ctx_before = (int)((int64_t)blk * nb_ctx / nb);
-        ctx_after = (int)((int64_t)(blk + 1) * nb_ctx / nb);
-    } else {
-        // Many decode units: the long context units start first, so none of
-        // them starts late; the short decode units fill the CUs after them.
-        ctx_before = min(blk, nb_ctx);
-        ctx_after = min(blk + 1, nb_ctx);
-    }
-    if (ctx_after > ctx_before) {
-        const int cid = ctx_before * XCDS + lane8;
+    const int nb_ctx = (n_ctx + XCDS - 1) / XCDS;
+    if (blk < nb_ctx) {
+        const int cid = blk * XCDS + lane8;
         if (cid < n_ctx) context_body<4>(c, cid, lds);
     } else {
         // Decode id -> (unit, row block): ids congruent mod 8 share an XCD;
         // the row blocks of a unit take consecutive ids of one residue.
-        const int did = (blk - ctx_before) * XCDS + lane8;
+        const int did = (blk - nb_ctx) * XCDS + lane8;
         const int rb = d.row_blocks;
         const int q = did / XCDS;
         const int unit = (q / rb) * XCDS + did % XCDS;
