@@ -177,7 +177,7 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
 // decode unit (sample, KV head), which also start together: the second
 // reads the decode rows the first brings into that XCD's L2 instead of
 // fetching them again.
-template <bool PAGED, bool PACK>
+template <bool PAGED, bool PACK, bool KEEP>
 __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextParams c, const PartialParams d,
                                                             int n_ctx, int n_dec) {
     __shared__ __attribute__((aligned(16))) char lds[CTX_LDS_BYTES];
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void bifurcated_kernel(const BifContextPara
         const int q = did / XCDS;
         const int unit = (q / rb) * XCDS + did % XCDS;
         if (did < n_dec && unit < d.B * d.Hkv)
-            partial_mfma_body<1, 4, PAGED, false, PACK>(d, unit * rb + q % rb,
+            partial_mfma_body<1, 4, PAGED, false, PACK, KEEP>(d, unit * rb + q % rb,
                                                        *reinterpret_cast<PartialLds<1, 4>*>(lds));
     }
 }
@@ -221,12 +221,23 @@ hipError_t launch_bifurcated(const BifContextParams& c, const PartialParams& d, 
     // role packs its weight remainders into the 16-row block's padding
     // columns (the paged form keeps two products per block: packing there
     // needs more registers than two workgroups per CU leave).
+    // With more than one row block per unit (groups above 16 heads), the
+    // blocks after the first read the unit's decode rows from L2, so those
+    // loads keep the default cache policy (read-once loads left the MQA
+    // workload fetching its decode rows twice).
     const bool pack = d.Hq / d.Hkv <= 8 && !d.block_table;
-#define FD_BIF(PG, PK) hipLaunchKernelGGL((bifurcated_kernel<PG, PK>), dim3((unsigned)wgs), dim3(256), 0, stream, c, d, \
-                                          (int)n_ctx, (int)n_dec)
-    if (d.block_table) FD_BIF(true, false);
-    else if (pack) FD_BIF(false, true);
-    else FD_BIF(false, false);
+    const bool keep = d.row_blocks > 1;
+#define FD_BIF(PG, PK, KP) hipLaunchKernelGGL((bifurcated_kernel<PG, PK, KP>), dim3((unsigned)wgs), dim3(256), 0, stream, \
+                                              c, d, (int)n_ctx, (int)n_dec)
+    if (d.block_table) {
+        if (keep) FD_BIF(true, false, true);
+        else FD_BIF(true, false, false);
+    } else if (pack) {
+        FD_BIF(false, true, false);
+    } else {
+        if (keep) FD_BIF(false, false, true);
+        else FD_BIF(false, false, false);
+    }
 #undef FD_BIF
     return hipGetLastError();
 }

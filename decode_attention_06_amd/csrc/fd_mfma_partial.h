@@ -59,6 +59,16 @@ __device__ __forceinline__ uint32_t row_off(const RowWindow& w, int token, uint3
     return __umul24((uint32_t)min(w.shift + token, w.lim), st32);
 }
 
+// KEEP: plain loads instead of read-once (non-temporal) ones, for rows that
+// another workgroup of the same XCD reads right after (the other row blocks
+// of a unit): they then come from L2.
+template <bool KEEP = false>
+__device__ __forceinline__ u32x4_t ld16_rows(const uint16_t* p) {
+    if constexpr (KEEP) return ld16(p);
+    else return ld16_kv(p);
+}
+
+template <bool KEEP = false>
 __device__ __forceinline__ void load_rows(const uint16_t* kpool, const uint16_t* vpool, int64_t ko, int64_t vo,
                                           int64_t st, int tb, int last, int ktok0, int g, int i, Bf16Tile& r) {
     const RowWindow w = row_window(tb, last);
@@ -69,14 +79,16 @@ __device__ __forceinline__ void load_rows(const uint16_t* kpool, const uint16_t*
     for (int blk = 0; blk < 2; ++blk) {
         const uint32_t off = row_off(w, ktok0 + 4 * blk, st32) + 8u * (uint32_t)g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16_kv(kt + off + 32 * s);
+        for (int s = 0; s < 4; ++s) r.k[blk][s] = ld16_rows<KEEP>(kt + off + 32 * s);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r.v[j] = ld16_kv(vt + (row_off(w, 8 * g + j, st32) + 8u * (uint32_t)i));
+    for (int j = 0; j < 8; ++j) r.v[j] = ld16_rows<KEEP>(vt + (row_off(w, 8 * g + j, st32) + 8u * (uint32_t)i));
 }
 
+template <bool KEEP = false>
 __device__ __forceinline__ void load_rows(const uint8_t* kpool, const uint8_t* vpool, int64_t ko, int64_t vo,
                                           int64_t st, int tb, int last, int ktok0, int g, int i, Fp8Tile& r) {
+    static_assert(!KEEP, "E4M3 caches are read once");
     const RowWindow w = row_window(tb, last);
     const uint8_t* kt = kpool + ko + (int64_t)w.tbase * st;
     const uint8_t* vt = vpool + vo + (int64_t)w.tbase * st;
@@ -156,7 +168,9 @@ struct PartialLds {
 
 // PACK: at most 8 query rows per unit (G <= 8, one 16-row block); the
 // weights' remainders ride in the block's padding columns (compute_tile).
-template <int NRB, int NW, bool PAGED = false, bool KV8 = false, bool PACK = false>
+// KEEP: the unit's KV rows are also read by its other row blocks (see
+// load_rows).
+template <int NRB, int NW, bool PAGED = false, bool KV8 = false, bool PACK = false, bool KEEP = false>
 __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bid, PartialLds<NRB, NW>& sh) {
     using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
     using Tile = typename std::conditional<KV8, Fp8Tile, Bf16Tile>::type;
@@ -263,11 +277,12 @@ __device__ __forceinline__ void partial_mfma_body(const PartialParams& p, int bi
             // then sits at offset + t * D).
             const int64_t o0 = kv_page_offset<MF_D>(p, ahead.id0, kvh, ahead.s0) - (int64_t)ahead.s0 * MF_D;
             const int64_t o1 = kv_page_offset<MF_D>(p, ahead.id1, kvh, ahead.s1) - (int64_t)ahead.s1 * MF_D;
-            load_rows(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, (int64_t)MF_D, at, t1 - 1, ktok0, g, i, r);
+            load_rows<KEEP>(kpool, vpool, i >= 8 ? o1 : o0, g >= 2 ? o1 : o0, (int64_t)MF_D, at, t1 - 1, ktok0, g, i,
+                            r);
             ahead = ahead2;
             ahead2 = paged_tile(p, b, at + 2 * step, t1 - 1);
         } else {
-            load_rows(kpool, vpool, slice, slice, p.kv_stride_t, at, t1 - 1, ktok0, g, i, r);
+            load_rows<KEEP>(kpool, vpool, slice, slice, p.kv_stride_t, at, t1 - 1, ktok0, g, i, r);
         }
     };
     int tb = t0 + wave * MF_TILE;
