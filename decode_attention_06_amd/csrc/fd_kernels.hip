@@ -678,19 +678,21 @@ __global__ __launch_bounds__(256) void lse_combine_v4_kernel(const float* __rest
 // short splits): one wave per row.  Lane j holds piece j's lse; the row
 // maximum and the weight sum are butterfly reductions (every lane ends with
 // the same bits); piece weights reach all lanes through v_readlane, and lane
-// j accumulates columns j, j + 64, ...  The first batch of pieces (32 for
-// head dims up to 128) is requested together with the lse values, so a row
-// of up to that many pieces costs one memory round trip.
+// j accumulates columns j, j + 64, ...  The first batch of PB pieces is
+// requested together with the lse values, so a row of up to that many pieces
+// costs one memory round trip.  PB is the smallest multiple of 8 that covers
+// the pieces (at most 64 loads in flight per lane): a batch past the last
+// piece re-reads it, so a tight batch saves those loads.
 constexpr int CMBW_ROWS = 4;                    // rows (waves) per workgroup
 constexpr int CMBW_MAXV = 8;                    // columns per lane: D <= 512
 
-template <int NV>
+template <int NV, int PB>
 __global__ __launch_bounds__(64 * CMBW_ROWS) void lse_combine_rows_kernel(const float* __restrict__ o_part,
                                                                           const float* __restrict__ lse_part,
                                                                           int32_t rows, int32_t n_parts, int32_t D,
                                                                           void* out, OutRows orows, int32_t out_bf16,
                                                                           float* lse_out) {
-    constexpr int PB = NV <= 2 ? 32 : (NV <= 4 ? 16 : 8);   // pieces per batch (64 loads in flight)
+    static_assert(PB * NV <= 64 && PB % 8 == 0, "pieces per batch");
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * CMBW_ROWS + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -831,12 +833,29 @@ hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int32_
         const dim3 grid((unsigned)((rows + CMBW_ROWS - 1) / CMBW_ROWS));
         const dim3 block(64 * CMBW_ROWS);
         const int nv = (head_dim + 63) / 64;
-#define FD_CMBW(NV_) hipLaunchKernelGGL(lse_combine_rows_kernel<NV_>, grid, block, 0, stream, o_part, lse_part, \
-                                        rows, n_parts, head_dim, out, orows, out_bf16, lse_out)
-        if (nv <= 1) FD_CMBW(1);
-        else if (nv == 2) FD_CMBW(2);
-        else if (nv <= 4) FD_CMBW(4);
-        else FD_CMBW(CMBW_MAXV);
+        const int pb8 = (n_parts + 7) / 8;   // batch of pieces, in eights
+#define FD_CMBW(NV_, PB_) hipLaunchKernelGGL((lse_combine_rows_kernel<NV_, PB_>), grid, block, 0, stream, o_part, \
+                                             lse_part, rows, n_parts, head_dim, out, orows, out_bf16, lse_out)
+        if (nv <= 2) {
+            if (pb8 <= 1) {
+                if (nv <= 1) FD_CMBW(1, 8);
+                else FD_CMBW(2, 8);
+            } else if (pb8 == 2) {
+                if (nv <= 1) FD_CMBW(1, 16);
+                else FD_CMBW(2, 16);
+            } else if (pb8 == 3) {
+                if (nv <= 1) FD_CMBW(1, 24);
+                else FD_CMBW(2, 24);
+            } else {
+                if (nv <= 1) FD_CMBW(1, 32);
+                else FD_CMBW(2, 32);
+            }
+        } else if (nv <= 4) {
+            if (pb8 <= 1) FD_CMBW(4, 8);
+            else FD_CMBW(4, 16);
+        } else {
+            FD_CMBW(CMBW_MAXV, 8);
+        }
 #undef FD_CMBW
         return hipGetLastError();
     }

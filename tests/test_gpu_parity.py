@@ -126,11 +126,13 @@ def test_bitwise_repeatable(fd):
 @pytest.mark.parametrize("rows,P,D", [(37, 19, 128), (5, 64, 128), (9, 65, 128), (4, 300, 128), (7, 3, 64),
                                       (6, 40, 100), (3, 70, 100), (2, 1, 128), (3, 17, 512),
                                       (1100, 40, 128), (1024, 64, 64), (1030, 17, 512), (1024, 33, 256),
-                                      (1025, 1, 128)])
+                                      (1025, 1, 128), (1024, 13, 128), (1027, 24, 128), (1024, 9, 64),
+                                      (1026, 20, 64), (1024, 7, 256)])
 def test_lse_combine_matches_oracle(fd, rows, P, D):
-    # >= 1024 rows with <= 64 pieces: one wave per row (batches of 32, 16 or
-    # 8 pieces by head dim, so 33..64 pieces take a second batch); otherwise
-    # the column-slice kernels
+    # >= 1024 rows with <= 64 pieces: one wave per row (batches of 8, 16, 24
+    # or 32 pieces, the smallest that covers the pieces within the head
+    # dim's limit, so 33..64 pieces take a second batch); otherwise the
+    # column-slice kernels
     rng = np.random.Generator(np.random.PCG64(12 + P))
     o = rng.standard_normal((rows, P, D)).astype(np.float32)
     lse = (rng.standard_normal((rows, P)) * 5).astype(np.float32)
