@@ -357,7 +357,11 @@ fd_status fd_bifurcated_attn(const void* q, const void* k_ctx, const void* v_ctx
  * PagedAttention paragraph: fixed-size blocks found through an indirection
  * table), as a serving cache keeps the rows every sample appends; the shared
  * context stays dense.  The result equals fd_bifurcated_attn on the gathered
- * decode cache bit for bit.
+ * decode cache: bit for bit for fp32 inputs and for more than 8 query heads
+ * per KV head; otherwise to within fp32 rounding of the row sums (with at
+ * most 8 query heads per KV head the dense decode part carries each weight's
+ * bf16 remainder in the padding columns of its matrix-core tile, which the
+ * paged form, short of registers, does not).
  *
  *   q, k_ctx, v_ctx, dec_lens, out, lse_out, scale: as in fd_bifurcated_attn
  *   k_pages, v_pages   [num_pages, Hkv, page_size, D]
