@@ -90,10 +90,10 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
     const float sl2 = p.scale_log2;
 
     f32x4_t acc[2][8], lacc[2];
-    float m[2];
+    RingRows rows;
+    ring_rows_init(rows);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        m[r] = -INFINITY;
         lacc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -127,7 +127,7 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
 #pragma unroll
             for (int st = 0; st < CTX_STAGES; ++st) {
                 const int t = t4 + st;
-                ring_tile(kr, vt, qb, c0 + t * CTX_TILE, c1, lim, g, sl2, m, lacc, acc);
+                ring_tile(kr, vt, qb, c0 + t * CTX_TILE, c1, lim, g, sl2, rows, lacc, acc);
                 if (t + 1 >= n_tiles) break;
                 wait_vm<TWO_TILES>();
                 ring_barrier();
@@ -159,7 +159,7 @@ __device__ __forceinline__ void context_body(const BifContextParams& p, int bid,
                 o.z = acc[r][e][2] * inv; o.w = acc[r][e][3] * inv;
                 *reinterpret_cast<float4*>(dst + 16 * e + 4 * g) = o;
             }
-            if (g == 0) p.lse_part[slot] = (lr > 0.f) ? (m[r] + __log2f(lr)) * kLn2f : -INFINITY;
+            if (g == 0) p.lse_part[slot] = (lr > 0.f) ? (rows.m[r] + __log2f(lr)) * kLn2f : -INFINITY;
         }
     }
 }

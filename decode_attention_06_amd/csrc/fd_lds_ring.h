@@ -135,16 +135,84 @@ __device__ __forceinline__ TileAddrs ring_step(const uint16_t* kbase, const uint
     return a;
 }
 
-// One ring tile for a wave's 32 query rows: scores, softmax step (masks as
-// in tile_softmax), then O^T += V^T P^T with the transposed V operands
-// (output row m of block e is d = 16e + m).
+// Online-softmax state of a wave's two 16-row blocks in the ring kernels.
+// `m` is the lazily raised reference (log2 domain, see tile_softmax); the
+// two derived values change only when it does, so they are kept instead of
+// being formed on every tile: `nref`, the weights' offset (-m, or 0 while
+// no score has been seen), and `thr`, the raw score above which the
+// reference must rise ((m + MF_RESCALE_SLACK) / sl2, or -inf while m is).
+struct RingRows {
+    float m[2];
+    float nref[2];
+    float thr[2];
+};
+
+__device__ __forceinline__ void ring_rows_init(RingRows& s) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        s.m[r] = -INFINITY;
+        s.nref[r] = 0.f;
+        s.thr[r] = -INFINITY;
+    }
+}
+
+// One ring tile for a wave's 32 query rows: scores, softmax step (masks,
+// the lazily raised reference and bf16 weights as in tile_softmax, the row
+// sums from the same weights on the matrix cores), then O^T += V^T P^T
+// with the transposed V operands (output row m of block e is d = 16e + m).
 __device__ __forceinline__ void ring_tile(const u32x4_t (&kr)[2][4], const u32x4_t (&vt)[8],
                                           const bf16x8_t (&qb)[2][4], int tb, int tmask, const int (&lim)[2], int g,
-                                          float sl2, float (&m)[2], f32x4_t (&lacc)[2], f32x4_t (&acc)[2][8]) {
+                                          float sl2, RingRows& st, f32x4_t (&lacc)[2], f32x4_t (&acc)[2][8]) {
+    const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4_t sc[2][2];
     tile_scores<2>(kr, qb, sc);
-    bf16x8_t pb[2], unused[2];
-    tile_softmax<2, false, f32x4_t>(sc, tb, tmask, lim, g, sl2, m, lacc, acc, pb, unused);
+    float t[2][8];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[r][j] = sc[r][j >> 2][j & 3];
+    // Masked tokens only in the tiles that reach tmask; the empty asm
+    // statements keep this a branch (see tile_softmax).
+    if (tb + MF_TILE > tmask) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (tb + 8 * g + j >= lim[r]) t[r][j] = -INFINITY;
+                asm volatile("" : "+v"(t[r][j]));
+            }
+    }
+    float mx[2];
+    bool raise = false;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        mx[r] = t[r][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx[r] = fmaxf(mx[r], t[r][j]);
+        raise = raise || (mx[r] > st.thr[r]);
+    }
+    if (__any(raise)) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float x = fmaxf(mx[r], __shfl_xor(mx[r], 16));
+            x = fmaxf(x, __shfl_xor(x, 32));
+            const float mn = fmaxf(st.m[r], x * sl2);
+            const float alpha = fast_exp2(st.m[r] - ((mn == -INFINITY) ? 0.f : mn));
+            lacc[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+            st.m[r] = mn;
+            st.nref[r] = (mn == -INFINITY) ? 0.f : -mn;
+            st.thr[r] = (mn == -INFINITY) ? -INFINITY : (mn + MF_RESCALE_SLACK) / sl2;
+        }
+    }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[r][j] = (__bf16)fast_exp2(fmaf(t[r][j], sl2, st.nref[r]));
+        lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[r], lacc[r], 0, 0, 0);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll

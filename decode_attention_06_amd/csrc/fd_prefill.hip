@@ -93,10 +93,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const float sl2 = p.scale_log2;
 
     f32x4_t acc[2][8], lacc[2];
-    float m[2];
+    RingRows rows;
+    ring_rows_init(rows);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        m[r] = -INFINITY;
         lacc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         for (int st = 0; st < CTX_STAGES; ++st) {
             const int t = t4 + st;
             const int tb = t * CTX_TILE;
-            if (wave_rows && tb <= w_last) ring_tile(kr, vt, qb, tb, w_first + 1, lim, g, sl2, m, lacc, acc);
+            if (wave_rows && tb <= w_last) ring_tile(kr, vt, qb, tb, w_first + 1, lim, g, sl2, rows, lacc, acc);
             if (t + 1 >= n_tiles) break;
             wait_vm<TWO_TILES>();
             ring_barrier();
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)   // d = 16e + 4g + ii
                     store_out(p.out, row * MF_D + 16 * e + 4 * g + ii, acc[r][e][ii] * inv, p.out_bf16);
-            if (g == 0 && p.lse_out) p.lse_out[row] = (lr > 0.f) ? (m[r] + __log2f(lr)) * kLn2f : -INFINITY;
+            if (g == 0 && p.lse_out) p.lse_out[row] = (lr > 0.f) ? (rows.m[r] + __log2f(lr)) * kLn2f : -INFINITY;
         }
     }
 }
