@@ -156,6 +156,19 @@ __device__ __forceinline__ void ring_rows_init(RingRows& s) {
     }
 }
 
+// Largest of eight scores in three v_max3_f32 and one v_max_f32.  Through
+// fmaxf the compiler first canonicalises two of the inputs (the scores come
+// straight from the matrix cores), two more instructions per row block;
+// the scores are never signalling NaNs, so the plain maxima are exact.
+__device__ __forceinline__ float max8(const float (&t)[8]) {
+    float a, b, c, d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(t[0]), "v"(t[1]), "v"(t[2]));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(b) : "v"(a), "v"(t[3]), "v"(t[4]));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(c) : "v"(b), "v"(t[5]), "v"(t[6]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(c), "v"(t[7]));
+    return d;
+}
+
 // One ring tile for a wave's 32 query rows: scores, softmax step (masks,
 // the lazily raised reference and bf16 weights as in tile_softmax, the row
 // sums from the same weights on the matrix cores), then O^T += V^T P^T
@@ -186,9 +199,7 @@ __device__ __forceinline__ void ring_tile(const u32x4_t (&kr)[2][4], const u32x4
     bool raise = false;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        mx[r] = t[r][0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx[r] = fmaxf(mx[r], t[r][j]);
+        mx[r] = max8(t[r]);
         raise = raise || (mx[r] > st.thr[r]);
     }
     if (__any(raise)) {
