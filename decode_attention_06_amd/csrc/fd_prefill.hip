@@ -15,9 +15,9 @@
 // unit streams K/V rows [0, end of its last position] through the LDS ring
 // (fd_lds_ring.h), every wave contracting each tile against its own rows.  A
 // wave skips the tiles past its last row and masks only the tiles that reach
-// its first row's position (the causal diagonal).  Units are dispatched
-// longest first, all (sequence, KV head) pairs of one position tile
-// together, so every XCD gets the same mix of long and short units.
+// its first row's position (the causal diagonal).  Units are dispatched so
+// that the position tiles of one (sequence, KV head) pair share an XCD and
+// run together where the pair count allows it, longest first (see below).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -45,13 +45,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, i = lane & 15;
 
-    // Units in dispatch order, longest (last position tile) first; the
-    // round-robin dispatch over the XCDs gives every XCD the same mix.
+    // Units in dispatch order.  Ids congruent mod 8 run on one XCD.  With
+    // the (sequence, KV head) pairs a multiple of 8, each XCD takes its
+    // pairs one after another, every pair's position tiles longest first:
+    // the units of one pair then run side by side and read the same KV
+    // rows through that XCD's L2.  Otherwise all pairs of one position tile
+    // go together, longest first, so every XCD gets the same mix.
     const int units = p.B * p.Hkv * p.n_ptiles;
     const int u = (int)blockIdx.x;
     if (u >= units) return;
-    const int ptile = p.n_ptiles - 1 - u / (p.B * p.Hkv);
-    const int bh = u % (p.B * p.Hkv);
+    const int nbh = p.B * p.Hkv;
+    int ptile, bh;
+    if (nbh % XCDS == 0) {
+        const int xcd = u % XCDS, idx = u / XCDS;
+        ptile = p.n_ptiles - 1 - idx % p.n_ptiles;
+        bh = (idx / p.n_ptiles) * XCDS + xcd;
+    } else {
+        ptile = p.n_ptiles - 1 - u / nbh;
+        bh = u % nbh;
+    }
     const int kvh = bh % p.Hkv, b = bh / p.Hkv;
     const int G = p.Hq / p.Hkv;
     const int PT = p.pos_per_tile;

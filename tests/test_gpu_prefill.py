@@ -28,6 +28,7 @@ SHAPES = [
     (1, 32, 2, 150, [150]),             # G = 16
     (1, 32, 1, 97, [97]),               # MQA, G = 32: 4 positions per unit
     (3, 4, 4, 33, [1, 32, 33]),         # short sequences, one tile
+    (4, 8, 4, 150, [150, 3, 64, 129]),  # 16 (sequence, KV head) pairs: two per XCD, ragged
 ]
 
 
