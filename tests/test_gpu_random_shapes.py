@@ -2,7 +2,8 @@
 
 Each case draws its own shape from its seed, within what the library
 supports: head dims 64 and 128, groups of 1-32 query heads per KV head,
-lengths from 1 row, any split count, page sizes 16-128, empty decode parts.
+lengths from 1 row, any split count, page sizes 16-128 (decode caches and
+the bifurcated decode part), empty decode parts.
 Outputs are fp32, so the comparison measures the computation alone
 (max-abs 1e-5 for fp32 inputs, 1e-2 for bf16 and E4M3 inputs); bf16
 outputs are the same values rounded once (test_gpu_output_rounding.py).
@@ -104,6 +105,26 @@ def test_random_bifurcated(fd, i):
                                   return_lse=True)
     torch.cuda.synchronize()
     ro, rl = oracle.bifurcated_attention(c["q"], c["k_ctx"], c["v_ctx"], c["k_dec"], c["v_dec"], c["dec_lens"])
+    assert max(max_abs(to_host(out), ro), max_abs(to_host(lse), rl)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_bifurcated_paged(fd, i):
+    d = Draw(75000 + i)
+    dt, D = d.pick(["fp32", "bf16"]), d.pick([64, 128])
+    (Hq, Hkv), S = d.heads(), d.int(1, 10)
+    Lc, Ld, ps = d.int(1, 2000), d.int(1, 200), d.pick([16, 32, 64, 128])
+    dl = [d.int(0, Ld) for _ in range(S)]
+    print(f"  bifurcated paged {dt} S{S} Hq{Hq} Hkv{Hkv} D{D} Lc{Lc} Ld{Ld} page {ps} dec{dl}", flush=True)
+    c = synth.bifurcated_case(S, Hq, Hkv, D, Lc, Ld, dt, seed=75000 + i, dec_lens=dl)
+    kp, vp, table = synth.paginate(c["k_dec"], c["v_dec"], c["dec_lens"], ps, seed=i)
+    t = {x: to_dev(c[x], dt) for x in ("q", "k_ctx", "v_ctx")}
+    out, lse = fd.bifurcated_attn_paged(t["q"], t["k_ctx"], t["v_ctx"], to_dev(kp, dt), to_dev(vp, dt),
+                                        torch.from_numpy(table).to("cuda"),
+                                        torch.from_numpy(c["dec_lens"]).to("cuda"), out_dtype=torch.float32,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.bifurcated_paged_attention(c["q"], c["k_ctx"], c["v_ctx"], kp, vp, table, c["dec_lens"])
     assert max(max_abs(to_host(out), ro), max_abs(to_host(lse), rl)) <= TOL[dt]
 
 
