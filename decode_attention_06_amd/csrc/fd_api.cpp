@@ -276,7 +276,7 @@ const char* fd_status_string(fd_status s) {
 
 const char* fd_last_error_message(void) { return g_err; }
 
-int32_t fd_version(void) { return 100; }
+int32_t fd_version(void) { return 200; }
 
 int32_t fd_plan_splits(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int64_t max_len, int32_t dtype, int32_t n_cu) {
